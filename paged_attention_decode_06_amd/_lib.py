@@ -1,0 +1,221 @@
+"""ctypes binding of libpa_decode.so (argument marshalling only).
+
+Every compute step runs in the HIP library; this module only turns torch
+tensors into pointers, sizes and the current HIP stream. It never falls back
+to another implementation: a missing library is an error.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpa_decode.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "pa_decode.h")
+
+PA_F32, PA_BF16 = 0, 1
+MODE_AUTO, MODE_V1, MODE_V2 = 0, 1, 2
+PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EALIGN, PA_EHIP = 0, -1, -2, -3, -4
+BLOCK_SIZE, PARTITION_SIZE, V2_THRESHOLD = 16, 512, 8192
+
+
+class PaShape(ctypes.Structure):
+    _fields_ = [
+        ("num_seqs", ctypes.c_int32),
+        ("num_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("max_blocks_per_seq", ctypes.c_int32),
+        ("num_blocks", ctypes.c_int64),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class PaError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: status {status} ({status_string(status)})")
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "pa_decode_v1": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_float, _P]),
+    "pa_decode_v2": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_float, _P, _P, _P, _P]),
+    "pa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_float, _P, _P, _P, _P]),
+    "pa_decode_partitions": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_float,
+                                            _P, _P, _P, ctypes.c_int, _P]),
+    "pa_lse_reduce": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_int, _P]),
+    "pa_decode_partitions_debug": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_float,
+                                                  _P, _P, _P, ctypes.c_int, _P, _P, _P]),
+    "pa_max_partitions": (ctypes.c_int64, [ctypes.POINTER(PaShape)]),
+    "pa_partials_elems": (ctypes.c_int64, [ctypes.POINTER(PaShape), ctypes.c_int]),
+    "pa_check_args": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), _P, _P, _P, ctypes.c_int]),
+    "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "pa_version": (ctypes.c_int, []),
+}
+
+
+def header_functions(path: str = HEADER) -> list[str]:
+    """Names of the functions include/pa_decode.h declares."""
+    text = open(path).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load the HIP library (once). Raises if it has not been built."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or os.environ.get("PA_DECODE_LIB", LIB_PATH)
+    if not os.path.exists(p):
+        raise RuntimeError(f"{p} is missing: build it first with "
+                           "`python -c 'import __graft_entry__ as g; g.build()'` "
+                           "or `python -m paged_attention_decode_06_amd._build`")
+    lib = ctypes.CDLL(p)
+    for name, (res, args) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().pa_status_string(int(status)).decode()
+
+
+def _dtype_code(dt) -> int:
+    import torch
+    if dt == torch.float32:
+        return PA_F32
+    if dt == torch.bfloat16:
+        return PA_BF16
+    raise PaError(PA_EUNSUPPORTED, f"dtype {dt}")
+
+
+def make_shape(q, k_cache, block_tables) -> PaShape:
+    """pa_shape from q [S, H, D], k_cache [NB, Hkv, 16, D], block_tables [S, MB]."""
+    S, H, D = q.shape
+    NB, Hkv, BS, D2 = k_cache.shape
+    if D2 != D:
+        raise PaError(PA_EINVAL, f"head_dim of q ({D}) and cache ({D2}) differ")
+    if block_tables.dim() != 2 or block_tables.shape[0] != S:
+        raise PaError(PA_EINVAL, "block_tables must be [num_seqs, max_blocks_per_seq]")
+    return PaShape(S, H, Hkv, D, BS, block_tables.shape[1], NB, _dtype_code(q.dtype))
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(int(getattr(stream, "cuda_stream", stream)))
+
+
+def _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens, partials=()):
+    import torch
+    ts = [t for t in (out, q, k_cache, v_cache, block_tables, seq_lens, *partials) if t is not None]
+    for t in ts:
+        if not t.is_cuda:
+            raise PaError(PA_EINVAL, "all tensors must be on the GPU")
+        if not t.is_contiguous():
+            raise PaError(PA_EINVAL, "all tensors must be contiguous")
+    if q is not None:
+        for t in (out, k_cache, v_cache):
+            if t.dtype != q.dtype:
+                raise PaError(PA_EINVAL, "q, caches and out must share one dtype")
+        if tuple(out.shape) != tuple(q.shape):
+            raise PaError(PA_EINVAL, "out must have q's shape")
+        if tuple(v_cache.shape) != tuple(k_cache.shape):
+            raise PaError(PA_EINVAL, "k_cache and v_cache shapes differ")
+    for t in (block_tables, seq_lens):
+        if t is not None and t.dtype != torch.int32:
+            raise PaError(PA_EINVAL, "block_tables and seq_lens must be int32")
+    for t in partials:
+        if t is not None and t.dtype != torch.float32:
+            raise PaError(PA_EINVAL, "partial buffers must be float32")
+
+
+def _call(name, rc):
+    if rc != PA_OK:
+        raise PaError(rc, name)
+
+
+def max_partitions(shape: PaShape) -> int:
+    r = load().pa_max_partitions(ctypes.byref(shape))
+    _call("pa_max_partitions", r if r < 0 else 0)
+    return int(r)
+
+
+def alloc_partials(shape: PaShape, device):
+    """(exp_sums, max_logits, tmp_out) float32 buffers sized for `shape`."""
+    import torch
+    P = max_partitions(shape)
+    S, H, D = shape.num_seqs, shape.num_heads, shape.head_dim
+    return (torch.empty((S, H, P), dtype=torch.float32, device=device),
+            torch.empty((S, H, P), dtype=torch.float32, device=device),
+            torch.empty((S, H, P, D), dtype=torch.float32, device=device))
+
+
+def pa_decode_v1(out, q, k_cache, v_cache, block_tables, seq_lens, scale, stream=None):
+    _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens)
+    sh = make_shape(q, k_cache, block_tables)
+    _call("pa_decode_v1", load().pa_decode_v1(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                              _ptr(block_tables), _ptr(seq_lens), ctypes.byref(sh),
+                                              float(scale), _stream(stream, q.device)))
+
+
+def _full(name, out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits, tmp_out, stream):
+    _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens, (exp_sums, max_logits, tmp_out))
+    sh = make_shape(q, k_cache, block_tables)
+    fn = getattr(load(), name)
+    _call(name, fn(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
+                   ctypes.byref(sh), float(scale), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out),
+                   _stream(stream, q.device)))
+
+
+def pa_decode_v2(out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits, tmp_out,
+                 stream=None):
+    _full("pa_decode_v2", out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits,
+          tmp_out, stream)
+
+
+def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits, tmp_out,
+              stream=None):
+    _full("pa_decode", out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits,
+          tmp_out, stream)
+
+
+def pa_decode_partitions(out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits,
+                         tmp_out, mode, stream=None):
+    _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens, (exp_sums, max_logits, tmp_out))
+    sh = make_shape(q, k_cache, block_tables)
+    _call("pa_decode_partitions", load().pa_decode_partitions(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
+        ctypes.byref(sh), float(scale), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), int(mode),
+        _stream(stream, q.device)))
+
+
+def pa_decode_partitions_debug(out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits,
+                               tmp_out, mode, gather_trace=None, err_flag=None, stream=None):
+    _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens, (exp_sums, max_logits, tmp_out))
+    sh = make_shape(q, k_cache, block_tables)
+    _call("pa_decode_partitions_debug", load().pa_decode_partitions_debug(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
+        ctypes.byref(sh), float(scale), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), int(mode),
+        _ptr(gather_trace), _ptr(err_flag), _stream(stream, q.device)))
+
+
+def pa_lse_reduce(out, exp_sums, max_logits, tmp_out, seq_lens, shape: PaShape, mode=MODE_V2, stream=None):
+    _check_tensors(out, None, None, None, None, seq_lens, (exp_sums, max_logits, tmp_out))
+    _call("pa_lse_reduce", load().pa_lse_reduce(_ptr(out), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out),
+                                                _ptr(seq_lens), ctypes.byref(shape), int(mode),
+                                                _stream(stream, out.device)))

@@ -266,3 +266,29 @@ def algorithmic_bytes(seq_lens, num_heads: int, num_kv_heads: int, head_dim: int
     qo = 2 * S * num_heads * head_dim * elem_bytes
     table = 4 * int(((lens + BLOCK_SIZE - 1) // BLOCK_SIZE).sum())
     return kv + qo + table + 4 * S
+
+
+def to_device(x: DecodeInputs, device="cuda"):
+    """Copy a workload to torch tensors on `device` (bf16 bit patterns become torch.bfloat16)."""
+    import torch
+
+    def conv(a):
+        if a.dtype == np.uint16:
+            return torch.from_numpy(a.view(np.int16)).to(device).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+    return {
+        "q": conv(x.q),
+        "k_cache": conv(x.k_cache),
+        "v_cache": conv(x.v_cache),
+        "block_tables": torch.from_numpy(x.block_tables).to(device),
+        "seq_lens": torch.from_numpy(x.seq_lens).to(device),
+    }
+
+
+def from_device(t) -> np.ndarray:
+    """Host float64 copy of a float32 or bfloat16 tensor."""
+    import torch
+    if t.dtype == torch.bfloat16:
+        return bf16_bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16)).astype(np.float64)
+    return t.float().cpu().numpy().astype(np.float64)

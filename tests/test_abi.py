@@ -1,0 +1,135 @@
+"""C-ABI checks that need no GPU: the library loads, exports what the header
+declares, and rejects every invalid argument with its documented status
+before touching the device."""
+import ctypes
+
+import pytest
+
+from paged_attention_decode_06_amd import _lib as L
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return L.load()
+
+
+def shape(**kw):
+    base = dict(num_seqs=2, num_heads=16, num_kv_heads=2, head_dim=128, block_size=16,
+                max_blocks_per_seq=100, num_blocks=1000, dtype=L.PA_BF16)
+    base.update(kw)
+    return L.PaShape(**base)
+
+
+A = 0x10000   # fake, well-aligned device addresses: validation never dereferences them
+
+
+def check(lib, sh, mode=L.MODE_AUTO, **ptrs):
+    p = dict(out=A, q=A, k=A, v=A, bt=A, sl=A, es=A, ml=A, to=A)
+    p.update(ptrs)
+    c = lambda x: None if x is None else ctypes.c_void_p(x)
+    return lib.pa_check_args(c(p["out"]), c(p["q"]), c(p["k"]), c(p["v"]), c(p["bt"]), c(p["sl"]),
+                             ctypes.byref(sh), c(p["es"]), c(p["ml"]), c(p["to"]), mode)
+
+
+def test_exports_every_header_function(lib):
+    names = L.header_functions()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.pa_version() == 1
+
+
+def test_header_constants_match_binding():
+    text = open(L.HEADER).read()
+    assert "#define PA_PARTITION_SIZE 512" in text
+    assert "#define PA_V2_THRESHOLD 8192" in text
+    assert "#define PA_BLOCK_SIZE 16" in text
+
+
+def test_valid_args_pass(lib):
+    assert check(lib, shape()) == L.PA_OK
+    assert check(lib, shape(dtype=L.PA_F32, head_dim=256, num_heads=2, num_kv_heads=1)) == L.PA_OK
+    # single pass needs no partial buffers
+    assert check(lib, shape(), L.MODE_V1, es=None, ml=None, to=None) == L.PA_OK
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(num_heads=15), L.PA_EINVAL),            # H % Hkv != 0
+    (dict(num_heads=0), L.PA_EINVAL),
+    (dict(num_kv_heads=0), L.PA_EINVAL),
+    (dict(num_seqs=-1), L.PA_EINVAL),
+    (dict(max_blocks_per_seq=0), L.PA_EINVAL),
+    (dict(num_blocks=0), L.PA_EINVAL),
+    (dict(head_dim=64), L.PA_EUNSUPPORTED),
+    (dict(head_dim=192), L.PA_EUNSUPPORTED),
+    (dict(block_size=32), L.PA_EUNSUPPORTED),
+    (dict(dtype=7), L.PA_EUNSUPPORTED),
+    (dict(num_heads=34, num_kv_heads=2), L.PA_EUNSUPPORTED),   # G = 17 > 16
+])
+def test_bad_shapes(lib, kw, status):
+    assert check(lib, shape(**kw)) == status
+
+
+def test_empty_batch_is_a_noop(lib):
+    assert check(lib, shape(num_seqs=0), out=None, q=None, k=None, v=None, bt=None, sl=None,
+                 es=None, ml=None, to=None) == L.PA_OK
+
+
+def test_bad_mode(lib):
+    assert check(lib, shape(), 9) == L.PA_EUNSUPPORTED
+
+
+@pytest.mark.parametrize("name", ["out", "q", "k", "v", "bt", "sl", "es", "ml", "to"])
+def test_null_pointers(lib, name):
+    assert check(lib, shape(), **{name: None}) == L.PA_EINVAL
+
+
+@pytest.mark.parametrize("name,addr", [("q", A + 8), ("k", A + 4), ("v", A + 2), ("out", A + 8),
+                                       ("to", A + 8), ("bt", A + 2), ("sl", A + 1), ("es", A + 2)])
+def test_misaligned(lib, name, addr):
+    assert check(lib, shape(), **{name: addr}) == L.PA_EALIGN
+
+
+def test_grid_limit(lib):
+    big = shape(num_seqs=1 << 20, max_blocks_per_seq=1 << 20)
+    assert check(lib, big) == L.PA_EUNSUPPORTED
+
+
+def test_entry_points_reject_before_launch(lib):
+    """Every entry point validates first: with a null q nothing reaches HIP."""
+    sh = shape()
+    n = None
+    a = ctypes.c_void_p(A)
+    assert lib.pa_decode(a, n, a, a, a, a, ctypes.byref(sh), 1.0, a, a, a, n) == L.PA_EINVAL
+    assert lib.pa_decode_v1(a, n, a, a, a, a, ctypes.byref(sh), 1.0, n) == L.PA_EINVAL
+    assert lib.pa_decode_v2(a, a, a, a, a, a, ctypes.byref(sh), 1.0, n, a, a, n) == L.PA_EINVAL
+    assert lib.pa_decode_partitions(a, n, a, a, a, a, ctypes.byref(sh), 1.0, a, a, a, 0, n) == L.PA_EINVAL
+    assert lib.pa_lse_reduce(a, n, a, a, a, ctypes.byref(sh), 2, n) == L.PA_EINVAL
+    bad = shape(head_dim=96)
+    assert lib.pa_lse_reduce(a, a, a, a, a, ctypes.byref(bad), 2, n) == L.PA_EUNSUPPORTED
+    assert lib.pa_decode_partitions_debug(a, a, a, a, a, a, ctypes.byref(sh), 1.0, a, a, a, 0,
+                                          ctypes.c_void_p(A + 2), n, n) == L.PA_EALIGN
+    assert lib.pa_decode(a, a, a, a, a, a, None, 1.0, a, a, a, n) == L.PA_EINVAL
+
+
+def test_partition_arithmetic(lib):
+    # Pmax = ceil(MB * 16 / 512): 6250 blocks (100000 tokens) -> 196 partitions
+    assert lib.pa_max_partitions(ctypes.byref(shape(max_blocks_per_seq=6250))) == 196
+    assert lib.pa_max_partitions(ctypes.byref(shape(max_blocks_per_seq=32))) == 1
+    assert lib.pa_max_partitions(ctypes.byref(shape(max_blocks_per_seq=33))) == 2
+    sh = shape(num_seqs=3, num_heads=16, max_blocks_per_seq=2048, head_dim=256)
+    assert lib.pa_partials_elems(ctypes.byref(sh), 0) == 3 * 16 * 64
+    assert lib.pa_partials_elems(ctypes.byref(sh), 1) == 3 * 16 * 64 * 256
+    assert lib.pa_partials_elems(ctypes.byref(sh), 5) == L.PA_EINVAL
+    assert lib.pa_max_partitions(ctypes.byref(shape(head_dim=5))) == L.PA_EUNSUPPORTED
+
+
+def test_status_strings(lib):
+    for st in (0, -1, -2, -3, -4):
+        assert lib.pa_status_string(st)
+    assert b"unknown" in lib.pa_status_string(-99)
+
+
+def test_library_missing_fails_loudly(tmp_path):
+    with pytest.raises(RuntimeError, match="missing"):
+        L.load(str(tmp_path / "nope.so"))
