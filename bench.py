@@ -1,0 +1,297 @@
+"""Benchmark: paged-attention decode on one MI355X.
+
+A step is one pa_decode call (per-sequence V1/V2 dispatch, partition kernel,
+log-sum-exp reduce kernel) over one batch of synthetic inputs already resident
+in HBM. Before every timed step a 1 GiB scrub *read* evicts the L2s and the
+256 MB Infinity Cache, so a workload that would fit there is still read from
+HBM; the scrub sits outside the timed window (events bracket the decode call
+only). A read scrub leaves no dirty lines behind: a 1 GiB write scrub was
+measured to slow the timed 100K-token step by ~18 us through write-backs that
+compete with the decode's reads. The default workload is the 100K-token decode (1 sequence, 16 query /
+2 KV heads, head_dim 128, bf16, 196 partitions of 512 tokens).
+
+Prints ONE JSON line (per workload with --all):
+  value        algorithmic bytes / mean event-timed step time, GB/s
+  ms_per_step  mean cold-cache step time (both kernels and the gap between)
+  roofline     the partition kernel's algorithmic bytes / its own mean
+               duration (HIP events around it alone), against 8 TB/s
+  cpu_baseline the fp64 oracle timed on this host's cores (bounded sample)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn decode achieved HBM GB/s (% of peak) + µs/step at 100K ctx"
+PEAK_GBS = 8000.0
+SCRUB_BYTES = 1 << 30
+KERNEL_SRC = os.path.join(ROOT, "paged_attention_decode_06_amd", "csrc", "pa_decode.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash() -> str:
+    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+
+
+def workload_label(x) -> dict:
+    c = x.cfg
+    lens = x.seq_lens
+    n_v2 = int((lens > 8192).sum())
+    return {
+        "workload": c.name,
+        "num_seqs": c.num_seqs, "num_heads": c.num_heads, "num_kv_heads": c.num_kv_heads,
+        "head_dim": c.head_dim, "block_size": 16, "cache_dtype": c.dtype,
+        "seq_lens": "x".join(map(str, lens.tolist())) if lens.size <= 4 else
+                    f"{c.lengths[0]}{list(c.lengths[1:])}: sum={int(lens.sum())} min={int(lens.min())} max={int(lens.max())}",
+        "seqs_on_v2": n_v2, "partition_size": 512, "v2_threshold": 8192,
+        "seed": x.seed,
+    }
+
+
+def partition_kernel_bytes(x, elem) -> int:
+    """Algorithmic bytes the partition kernel must move: K and V of every
+    context token per KV head (2 * D * elem), q, the table entries and
+    seq_lens, and the out rows of single-pass sequences."""
+    from paged_attention_decode_06_amd import workloads as W
+    c = x.cfg
+    total = W.algorithmic_bytes(x.seq_lens, c.num_heads, c.num_kv_heads, c.head_dim, elem)
+    v2_rows = int((x.seq_lens > 8192).sum()) * c.num_heads * c.head_dim * elem
+    return total - v2_rows        # out of V2 rows is written by the reduce kernel
+
+
+def traffic_for(num: int):
+    """HBM traffic per launch from committed counter runs, when they were taken
+    on the current kernel source; otherwise None."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    ent = rec.get("workloads", {}).get(str(num))
+    return None if ent is None else ent.get("partition_kernel_bytes_per_launch")
+
+
+def cpu_baseline(x, gpu_out, budget_s: float):
+    """Time the fp64 oracle on host cores over a bounded sample of the workload:
+    whole sequences in a fixed random order until the time budget is spent
+    (the workload is repeated when it is shorter than the budget)."""
+    import oracle
+    from paged_attention_decode_06_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        blas = 1
+    c = x.cfg
+    lists = oracle.gather_list(x.block_tables, x.seq_lens)
+    order = np.random.default_rng(0).permutation(c.num_seqs)
+    got = W.from_device(gpu_out)
+    elapsed, sample_bytes, tokens, visits, reps, worst = 0.0, 0, 0, 0, 0, 0.0
+    checked = set()
+    while elapsed < budget_s and reps < 50:
+        for s in order:
+            L = int(x.seq_lens[s])
+            t0 = time.perf_counter()
+            ref = oracle.attend_seq(x.q[s], x.k_cache, x.v_cache, lists[s], L, x.scale, c.dtype)
+            elapsed += time.perf_counter() - t0
+            if s not in checked:
+                worst = max(worst, float(np.abs(got[s] - ref).max()))
+                checked.add(int(s))
+            sample_bytes += W.algorithmic_bytes([L], c.num_heads, c.num_kv_heads, c.head_dim,
+                                                4 if c.dtype == "f32" else 2)
+            tokens += L
+            visits += 1
+            if elapsed >= budget_s:
+                break
+        reps += 1
+    return {
+        "value": round(sample_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(blas), "kind": "oracle",
+        "sample": f"fp64 NumPy oracle over {visits} sequence visits ({len(checked)} distinct of {c.num_seqs}, "
+                  f"{tokens} context tokens) in {elapsed:.1f} s; BLAS threads={blas}, "
+                  "gather/softmax loop single-threaded",
+        "seconds": round(elapsed, 3),
+        "max_abs_err_vs_gpu": worst,
+    }
+
+
+def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float, dev):
+    import torch
+
+    import paged_attention_decode_06_amd as pa
+    from paged_attention_decode_06_amd import workloads as W
+
+    t0 = time.time()
+    x = W.make_inputs(num)
+    log(f"[bench] config {num} {x.cfg.name}: inputs drawn in {time.time() - t0:.1f}s; "
+        f"sum(L)={int(x.seq_lens.sum())}")
+    d = W.to_device(x, dev)
+    q, kc, vc, bt, sl = d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens"]
+    out = torch.empty_like(q)
+    sh = pa.make_shape(q, kc, bt)
+    es, ml, to = pa.alloc_partials(sh, dev)
+    elem = 4 if x.cfg.dtype == "f32" else 2
+    step_bytes = W.algorithmic_bytes(x.seq_lens, x.cfg.num_heads, x.cfg.num_kv_heads, x.cfg.head_dim, elem)
+    pk_bytes = partition_kernel_bytes(x, elem)
+    scrub_buf = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        pa.pa_decode(out, q, kc, vc, bt, sl, x.scale, es, ml, to, stream=stream)
+
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+
+    def do_scrub(i):
+        if scrub:
+            torch.sum(scrub_buf, dim=None, out=sink)
+
+    for i in range(warmup):
+        do_scrub(i)
+        step()
+    torch.cuda.synchronize(dev)
+
+    # --- timed region: K steps, each bracketed by events (scrub outside the events)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize(dev)
+    wall0 = time.perf_counter()
+    for i in range(steps):
+        do_scrub(i)
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    wall = time.perf_counter() - wall0
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    # --- per-kernel durations: the same step split at the kernel boundary
+    ev3 = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
+    for i in range(steps):
+        do_scrub(i)
+        ev3[i][0].record(stream)
+        pa.pa_decode_partitions(out, q, kc, vc, bt, sl, x.scale, es, ml, to, pa.MODE_AUTO, stream=stream)
+        ev3[i][1].record(stream)
+        pa.pa_lse_reduce(out, es, ml, to, sl, sh, pa.MODE_AUTO, stream=stream)
+        ev3[i][2].record(stream)
+    torch.cuda.synchronize(dev)
+    k1 = np.array([a.elapsed_time(b) for a, b, _ in ev3])
+    k2 = np.array([b.elapsed_time(c) for _, b, c in ev3])
+
+    # --- pipelined figure: [scrub, step] x K back to back minus [scrub] x K
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    e0.record(stream)
+    for i in range(steps):
+        do_scrub(i)
+        step()
+    e1.record(stream)
+    for i in range(steps):
+        do_scrub(i)
+    e2.record(stream)
+    torch.cuda.synchronize(dev)
+    pipelined_ms = (e0.elapsed_time(e1) - e1.elapsed_time(e2)) / steps
+
+    # --- warm (cache-resident) figure, labelled as such
+    evw = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        evw[i][0].record(stream)
+        step()
+        evw[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    warm = np.array([a.elapsed_time(b) for a, b in evw])
+
+    ms_step = float(ms.mean())
+    gbs = step_bytes / (ms_step * 1e-3) / 1e9
+    k1_ms = float(k1.mean())
+    achieved = pk_bytes / (k1_ms * 1e-3) / 1e9
+    res = {
+        "metric": METRIC,
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": x.cfg.dtype,
+        "data": "synthetic",
+        "config": workload_label(x),
+        "us_per_step": round(ms_step * 1e3, 2),
+        "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
+        "us_per_step_p10_p50_p90": [round(float(np.percentile(ms, p)) * 1e3, 2) for p in (10, 50, 90)],
+        "cache_scrub_bytes_per_step": SCRUB_BYTES if scrub else 0,
+        "warm_cache_us_per_step": round(float(warm.mean()) * 1e3, 2),
+        "pipelined_us_per_step": round(pipelined_ms * 1e3, 2),
+        "algorithmic_bytes_per_step": int(step_bytes),
+        "seq_steps_per_s": round(x.cfg.num_seqs / (ms_step * 1e-3), 1),
+        "context_tokens_per_s": round(float(x.seq_lens.sum()) / (ms_step * 1e-3), 1),
+        "wall_s_timed_region_incl_scrub": round(wall, 4),
+        "kernels_us_mean": {"pa_partition": round(k1_ms * 1e3, 2), "pa_lse_reduce": round(float(k2.mean()) * 1e3, 2)},
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBS, 4),
+            "traffic": traffic_for(num),
+            "kernel": "pa_partition",
+            "algorithmic_bytes_per_launch": int(pk_bytes),
+        },
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    if cpu_budget > 0:
+        log(f"[bench] config {num}: timing the fp64 oracle (~{cpu_budget:.0f}s budget)")
+        res["cpu_baseline"] = cpu_baseline(x, out, cpu_budget)
+    else:
+        res["cpu_baseline"] = None
+    del scrub_buf
+    return res
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", type=int, default=3, help="workload number 1..5 (default 3: 100K context)")
+    ap.add_argument("--all", action="store_true", help="every workload, one JSON line each")
+    ap.add_argument("--no-scrub", action="store_true", help="skip the cache scrub (warm-cache timing)")
+    ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0 = skip)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the decode path runs on a single MI355X and has no "
+              "multi-GPU mode (see the sharding notes in the design document). Run with --gpus 1.",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    import paged_attention_decode_06_amd as pa
+    pa.load()
+    dev = torch.device("cuda:0")
+    nums = [1, 2, 3, 4, 5] if args.all else [args.config]
+    for n in nums:
+        res = bench_one(n, args.steps, args.warmup, not args.no_scrub, args.cpu_budget, dev)
+        print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -16,6 +16,9 @@ pytestmark = pytest.mark.gpu
 
 TOL = {"f32": 1e-3, "bf16": 2e-2}
 MODES = ("auto", "v1", "v2")
+# Table widths: the natural one, and 4096 blocks, which gives 128 partitions
+# per sequence and so exercises the one-partition-per-wave launch layout.
+WIDTHS = (None, 4096)
 
 
 @pytest.fixture(scope="module")
@@ -107,12 +110,13 @@ def test_config_parity(dev, num):
 MIXED = [1, 37, 512, 513, 5000, 8192, 8193, 20000]
 
 
+@pytest.mark.parametrize("width", WIDTHS)
 @pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("mode", MODES)
-def test_modes_vs_oracle(dev, D, mode):
+def test_modes_vs_oracle(dev, D, mode, width):
     cfg = W.DecodeConfig(f"mixed-d{D}", len(MIXED), 16, 2, D, "bf16", ("custom",))
-    x = W.make_inputs(cfg, seed=11, seq_lens=MIXED)
-    say(f"mode {mode} D={D} lens={MIXED}")
+    x = W.make_inputs(cfg, seed=11, seq_lens=MIXED, max_blocks_per_seq=width)
+    say(f"mode {mode} D={D} lens={MIXED} table width={x.max_blocks_per_seq}")
     out, _ = run(x, dev, mode)
     assert_close(x, out, label=mode)
 
@@ -178,11 +182,12 @@ def test_empty_batch(dev):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("width", [600, 4096])
 @pytest.mark.parametrize("mode", MODES)
-def test_poison_outside_contexts_never_reaches_output(dev, dtype, mode):
+def test_poison_outside_contexts_never_reaches_output(dev, dtype, mode, width):
     lens = [37, 1, 8200, 700]
     cfg = W.DecodeConfig(f"poison-{dtype}", len(lens), 16, 2, 128, dtype, ("custom",))
-    x = W.make_inputs(cfg, seed=16, seq_lens=lens, max_blocks_per_seq=600, poison=True)
+    x = W.make_inputs(cfg, seed=16, seq_lens=lens, max_blocks_per_seq=width, poison=True)
     say(f"poisoned pool {dtype} mode={mode}")
     out, _ = run(x, dev, mode)
     got = assert_close(x, out, label=mode)
@@ -248,10 +253,11 @@ def test_zero_query_gives_mean_of_v(dev):
 
 
 # ---------------------------------------------------------------- gather trace, partials, dispatch
+@pytest.mark.parametrize("width", [1300, 4096])
 @pytest.mark.parametrize("mode", MODES)
-def test_gather_trace_matches_oracle_exactly(dev, mode):
-    lens = [37, 1, 8192, 8193, 20000, 513]
-    x = W.make_inputs(W.CONFIGS[2], seed=22, seq_lens=lens, max_blocks_per_seq=1300, poison=True)
+def test_gather_trace_matches_oracle_exactly(dev, mode, width):
+    lens = [37, 1, 8192, 8193, 20000, 513, 40000, 9000]
+    x = W.make_inputs(W.CONFIGS[2], seed=22, seq_lens=lens, max_blocks_per_seq=max(width, 2500), poison=True)
     d = W.to_device(x, dev)
     sh = pa.make_shape(d["q"], d["k_cache"], d["block_tables"])
     es, ml, to = pa.alloc_partials(sh, dev)
@@ -270,9 +276,10 @@ def test_gather_trace_matches_oracle_exactly(dev, mode):
     assert int(err.item()) == 0
 
 
-def test_partials_match_oracle_partition_stats(dev):
+@pytest.mark.parametrize("width", WIDTHS)
+def test_partials_match_oracle_partition_stats(dev, width):
     lens = [1100, 513, 9000, 1]
-    x = W.make_inputs(W.CONFIGS[2], seed=23, seq_lens=lens)
+    x = W.make_inputs(W.CONFIGS[2], seed=23, seq_lens=lens, max_blocks_per_seq=width)
     d = W.to_device(x, dev)
     sh = pa.make_shape(d["q"], d["k_cache"], d["block_tables"])
     es, ml, to = pa.alloc_partials(sh, dev)
@@ -294,11 +301,18 @@ def test_partials_match_oracle_partition_stats(dev):
         assert np.isnan(ml[s, :, P:]).all() and np.isnan(to[s, :, P:]).all()   # untouched
 
 
+# (S, H, D): the reduce picks its slice width from S * H rows; these reach the
+# 32-, 64-, 128- and 256-wide slices.
+REDUCE_SHAPES = [(3, 4, 128), (64, 16, 128), (128, 16, 128), (128, 16, 256)]
+
+
+@pytest.mark.parametrize("S,H,D", REDUCE_SHAPES)
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
-def test_reduce_fed_with_oracle_partials(dev, dtype):
+def test_reduce_fed_with_oracle_partials(dev, dtype, S, H, D):
     rng = np.random.default_rng(24)
-    S, H, D, MB = 3, 4, 128, 100          # Pmax = ceil(100*16/512) = 4
-    lens = np.array([1600, 1500, 100], np.int32)
+    MB = 100                               # Pmax = ceil(100*16/512) = 4
+    lens = rng.integers(1, 1601, size=S).astype(np.int32)
+    lens[0] = 1600
     P = 4
     m = rng.normal(0, 5, (S, H, P)); l = rng.uniform(1, 50, (S, H, P)); o = rng.normal(0, 1, (S, H, P, D))
     want = np.zeros((S, H, D))
@@ -310,15 +324,16 @@ def test_reduce_fed_with_oracle_partials(dev, dtype):
     out = torch.full((S, H, D), float("nan"), dtype=tdt, device=dev)
     to_t = lambda a: torch.from_numpy(a.astype(np.float32)).to(dev)
     sh = pa.PaShape(S, H, 1, D, 16, MB, 10, pa.PA_BF16 if dtype == "bf16" else pa.PA_F32)
-    say(f"reduce from oracle partials {dtype}")
+    say(f"reduce from oracle partials {dtype} S={S} H={H} D={D}")
     pa.pa_lse_reduce(out, to_t(l), to_t(m), to_t(o), torch.from_numpy(lens).to(dev), sh, pa.MODE_V2)
     torch.cuda.synchronize(dev)
     assert max_err(W.from_device(out), want) <= (2e-2 if dtype == "bf16" else 1e-5)
 
 
-def test_auto_writes_partials_only_for_long_contexts(dev):
+@pytest.mark.parametrize("width", WIDTHS)
+def test_auto_writes_partials_only_for_long_contexts(dev, width):
     lens = [37, 8192, 8193, 20000, 600]
-    x = W.make_inputs(W.CONFIGS[2], seed=25, seq_lens=lens)
+    x = W.make_inputs(W.CONFIGS[2], seed=25, seq_lens=lens, max_blocks_per_seq=width)
     d = W.to_device(x, dev)
     sh = pa.make_shape(d["q"], d["k_cache"], d["block_tables"])
     es, ml, to = pa.alloc_partials(sh, dev)
