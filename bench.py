@@ -13,9 +13,17 @@ compete with the decode's reads. The default workload is the 100K-token decode (
 Prints ONE JSON line (per workload with --all):
   value        algorithmic bytes / mean event-timed step time, GB/s
   ms_per_step  mean cold-cache step time (both kernels and the gap between)
-  roofline     the partition kernel's algorithmic bytes / its own mean
-               duration (HIP events around it alone), against 8 TB/s
+  roofline     the partition kernel's algorithmic bytes / its mean duration,
+               against 8 TB/s. The duration comes from HIP events on the
+               launch stream around K back-to-back [scrub, kernel] pairs minus
+               K scrubs alone, so it excludes the event markers' own latency
+               and matches the profiler's per-dispatch duration.
   cpu_baseline the fp64 oracle timed on this host's cores (bounded sample)
+
+--cold-only runs just the warmup and the timed scrubbed steps (for a
+profiler run whose per-dispatch averages then cover cold calls only);
+--copy-calibration MiB runs a plain device-to-device copy of that size, the
+reference for scaling the FETCH_SIZE / WRITE_SIZE counters.
 """
 from __future__ import annotations
 
@@ -36,7 +44,7 @@ METRIC = "paged-attn decode achieved HBM GB/s (% of peak) + µs/step at 100K ctx
 PEAK_GBS = 8000.0
 SCRUB_BYTES = 1 << 30
 KERNEL_SRC = os.path.join(ROOT, "paged_attention_decode_06_amd", "csrc", "pa_decode.hip")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 
 
 def log(*a):
@@ -73,17 +81,29 @@ def partition_kernel_bytes(x, elem) -> int:
     return total - v2_rows        # out of V2 rows is written by the reduce kernel
 
 
-def traffic_for(num: int):
-    """HBM traffic per launch from committed counter runs, when they were taken
-    on the current kernel source; otherwise None."""
+def read_traffic_file(path: str = TRAFFIC_FILE) -> dict:
+    """`key: value` lines of the committed counter summary (text)."""
+    rec = {}
     try:
-        rec = json.load(open(TRAFFIC_FILE))
-    except (OSError, ValueError):
-        return None
+        for line in open(path):
+            line = line.split("#", 1)[0].strip()
+            if ":" in line:
+                k, v = line.split(":", 1)
+                rec[k.strip()] = v.strip()
+    except OSError:
+        pass
+    return rec
+
+
+def traffic_for(num: int):
+    """Calibrated HBM bytes (FETCH + WRITE) per partition-kernel launch from the
+    committed counter runs, when they were taken on the current kernel source;
+    otherwise None."""
+    rec = read_traffic_file()
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    ent = rec.get("workloads", {}).get(str(num))
-    return None if ent is None else ent.get("partition_kernel_bytes_per_launch")
+    v = rec.get(f"workload_{num}_partition_traffic_bytes")
+    return None if v is None else int(float(v))
 
 
 def cpu_baseline(x, gpu_out, budget_s: float):
@@ -103,7 +123,7 @@ def cpu_baseline(x, gpu_out, budget_s: float):
     got = W.from_device(gpu_out)
     elapsed, sample_bytes, tokens, visits, reps, worst = 0.0, 0, 0, 0, 0, 0.0
     checked = set()
-    while elapsed < budget_s and reps < 50:
+    while elapsed < budget_s and reps < 1000:
         for s in order:
             L = int(x.seq_lens[s])
             t0 = time.perf_counter()
@@ -129,7 +149,7 @@ def cpu_baseline(x, gpu_out, budget_s: float):
     }
 
 
-def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float, dev):
+def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float, dev, cold_only=False):
     import torch
 
     import paged_attention_decode_06_amd as pa
@@ -176,32 +196,34 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - wall0
     ms = np.array([a.elapsed_time(b) for a, b in ev])
+    if cold_only:
+        return {"config": workload_label(x), "us_per_step": round(float(ms.mean()) * 1e3, 2)}
 
-    # --- per-kernel durations: the same step split at the kernel boundary
-    ev3 = [tuple(torch.cuda.Event(enable_timing=True) for _ in range(3)) for _ in range(steps)]
-    for i in range(steps):
-        do_scrub(i)
-        ev3[i][0].record(stream)
+    # --- per-kernel durations: K back-to-back [scrub, work] launches minus
+    #     K scrubs alone, all bracketed by events on the launch stream
+    def partitions():
         pa.pa_decode_partitions(out, q, kc, vc, bt, sl, x.scale, es, ml, to, pa.MODE_AUTO, stream=stream)
-        ev3[i][1].record(stream)
-        pa.pa_lse_reduce(out, es, ml, to, sl, sh, pa.MODE_AUTO, stream=stream)
-        ev3[i][2].record(stream)
-    torch.cuda.synchronize(dev)
-    k1 = np.array([a.elapsed_time(b) for a, b, _ in ev3])
-    k2 = np.array([b.elapsed_time(c) for _, b, c in ev3])
 
-    # --- pipelined figure: [scrub, step] x K back to back minus [scrub] x K
-    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-    e0.record(stream)
-    for i in range(steps):
-        do_scrub(i)
-        step()
-    e1.record(stream)
-    for i in range(steps):
-        do_scrub(i)
-    e2.record(stream)
-    torch.cuda.synchronize(dev)
-    pipelined_ms = (e0.elapsed_time(e1) - e1.elapsed_time(e2)) / steps
+    def reduce():
+        pa.pa_lse_reduce(out, es, ml, to, sl, sh, pa.MODE_AUTO, stream=stream)
+
+    def pipelined(*work):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        for i in range(steps):
+            do_scrub(i)
+            for w in work:
+                w()
+        e[1].record(stream)
+        for i in range(steps):
+            do_scrub(i)
+        e[2].record(stream)
+        torch.cuda.synchronize(dev)
+        return (e[0].elapsed_time(e[1]) - e[1].elapsed_time(e[2])) / steps
+
+    k1_ms = pipelined(partitions)
+    pipelined_ms = pipelined(partitions, reduce)
+    k2_ms = max(pipelined_ms - k1_ms, 0.0)
 
     # --- warm (cache-resident) figure, labelled as such
     evw = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
@@ -214,7 +236,6 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
 
     ms_step = float(ms.mean())
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
-    k1_ms = float(k1.mean())
     achieved = pk_bytes / (k1_ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
@@ -240,7 +261,8 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
         "seq_steps_per_s": round(x.cfg.num_seqs / (ms_step * 1e-3), 1),
         "context_tokens_per_s": round(float(x.seq_lens.sum()) / (ms_step * 1e-3), 1),
         "wall_s_timed_region_incl_scrub": round(wall, 4),
-        "kernels_us_mean": {"pa_partition": round(k1_ms * 1e3, 2), "pa_lse_reduce": round(float(k2.mean()) * 1e3, 2)},
+        "kernels_us_mean": {"pa_partition": round(k1_ms * 1e3, 2), "pa_lse_reduce": round(k2_ms * 1e3, 2),
+                            "method": "K x [scrub, kernel] minus K x [scrub], HIP events on the launch stream"},
         "roofline": {
             "bound": "hbm",
             "achieved": round(achieved, 2),
@@ -271,6 +293,9 @@ def main(argv=None):
     ap.add_argument("--all", action="store_true", help="every workload, one JSON line each")
     ap.add_argument("--no-scrub", action="store_true", help="skip the cache scrub (warm-cache timing)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0 = skip)")
+    ap.add_argument("--cold-only", action="store_true", help="only warmup + timed scrubbed steps (profiler runs)")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args(argv)
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -283,12 +308,21 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
+    dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize(dev)
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return 0
     import paged_attention_decode_06_amd as pa
     pa.load()
-    dev = torch.device("cuda:0")
     nums = [1, 2, 3, 4, 5] if args.all else [args.config]
     for n in nums:
-        res = bench_one(n, args.steps, args.warmup, not args.no_scrub, args.cpu_budget, dev)
+        res = bench_one(n, args.steps, args.warmup, not args.no_scrub, args.cpu_budget, dev, args.cold_only)
         print(json.dumps(res), flush=True)
     return 0
 
