@@ -289,7 +289,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", type=int, default=3, help="workload number 1..5 (default 3: 100K context)")
+    ap.add_argument("--config", type=int, default=3,
+                    help="workload number 1..6 (default 3: 100K context, bf16; 6: the same with fp16)")
     ap.add_argument("--all", action="store_true", help="every workload, one JSON line each")
     ap.add_argument("--no-scrub", action="store_true", help="skip the cache scrub (warm-cache timing)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0 = skip)")

@@ -60,9 +60,9 @@ extern "C" {
 #endif
 
 /* Element type shared by q, the caches and out. [prefix-doc] model attention
- * shapes: the served model runs its attention in 16-bit floats (bf16 here);
- * f32 is the exact-arithmetic variant. */
-typedef enum { PA_F32 = 0, PA_BF16 = 1 } pa_dtype;
+ * shapes: the served model runs its attention in fp16 or bf16; f32 is the
+ * exact-arithmetic variant. */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
 
 /* Path selection for pa_decode_partitions / pa_lse_reduce. */
 typedef enum {

@@ -31,9 +31,11 @@ V2_THRESHOLD = 8192    # [cd0d9e1a] paged_attn.py rewrite, item 2: contexts long
 
 
 def widen(a: np.ndarray, dtype: str) -> np.ndarray:
-    """Exact float64 view of stored values ("f32" floats or "bf16" uint16 bit patterns)."""
+    """Exact float64 view of stored values ("f32" / "f16" floats or "bf16" uint16 bit patterns)."""
     if dtype == "f32":
         return np.asarray(a, dtype=np.float32).astype(np.float64)
+    if dtype == "f16":
+        return np.asarray(a, dtype=np.float16).astype(np.float64)
     if dtype == "bf16":
         bits = np.asarray(a, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
         return bits.view(np.float32).astype(np.float64)

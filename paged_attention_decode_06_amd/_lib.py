@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpa_decode.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "pa_decode.h")
 
-PA_F32, PA_BF16 = 0, 1
+PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 MODE_AUTO, MODE_V1, MODE_V2 = 0, 1, 2
 PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EALIGN, PA_EHIP = 0, -1, -2, -3, -4
 BLOCK_SIZE, PARTITION_SIZE, V2_THRESHOLD = 16, 512, 8192
@@ -95,6 +95,8 @@ def _dtype_code(dt) -> int:
         return PA_F32
     if dt == torch.bfloat16:
         return PA_BF16
+    if dt == torch.float16:
+        return PA_F16
     raise PaError(PA_EUNSUPPORTED, f"dtype {dt}")
 
 

@@ -46,6 +46,9 @@ constexpr int kReduceThreads = 256;
 constexpr int kReduceChunk = 32;   // head dims per reduce workgroup
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -156,6 +159,35 @@ __device__ __forceinline__ void store4_partial(float* row, int d, f32x4 v) {
   asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(row + d), "v"(v) : "memory");
 }
 
+// 16-bit element types of the cache: operand vectors and the two MFMA shapes
+// the partition kernel uses (16x16x32 for QK and two-block P.V, 16x16x16 for
+// one-block P.V). bf16 and fp16 share every lane layout.
+template <typename T>
+struct H16;
+template <>
+struct H16<__bf16> {
+  typedef bf16x8 x8;
+  typedef bf16x4 x4;
+  static __device__ __forceinline__ f32x4 mma32(x8 a, x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(x4 a, x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), __builtin_bit_cast(i16x4, b),
+                                                      c, 0, 0, 0);
+  }
+};
+template <>
+struct H16<_Float16> {
+  typedef f16x8 x8;
+  typedef f16x4 x4;
+  static __device__ __forceinline__ f32x4 mma32(x8 a, x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(x4 a, x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16f16(a, b, c, 0, 0, 0);
+  }
+};
+
 // Store 4 consecutive head dims starting at dim d of head g.
 template <typename T>
 __device__ __forceinline__ void store4(T* row, int d, f32x4 v);
@@ -165,13 +197,21 @@ __device__ __forceinline__ void store4<float>(float* row, int d, f32x4 v) {
 }
 template <>
 __device__ __forceinline__ void store4<__bf16>(__bf16* row, int d, f32x4 v) {
-  typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
   bf16x4 b;
   b[0] = (__bf16)v[0];
   b[1] = (__bf16)v[1];
   b[2] = (__bf16)v[2];
   b[3] = (__bf16)v[3];
   *reinterpret_cast<bf16x4*>(row + d) = b;
+}
+template <>
+__device__ __forceinline__ void store4<_Float16>(_Float16* row, int d, f32x4 v) {
+  f16x4 b;
+  b[0] = (_Float16)v[0];
+  b[1] = (_Float16)v[1];
+  b[2] = (_Float16)v[2];
+  b[3] = (_Float16)v[3];
+  *reinterpret_cast<f16x4*>(row + d) = b;
 }
 
 // Merge the per-wave (max, exp-sum, output) triples of one workgroup and
@@ -265,22 +305,22 @@ __device__ __forceinline__ void write_zeros(const Params& P, int s, int kvh, int
 // VGPR (lane j holds one id) and reads them with readlane, so no tile waits on
 // a table load of its own.
 template <int D, int TB>
-struct BTile {
+struct BTile {  // element-type agnostic: raw 16-byte chunks
   static constexpr int NH = D / 128;
   u32x4 k[TB][4][NH];  // K[4*grp + rr][128h + 8g .. +8]
   u32x4 v[TB][4][NH];  // V[4*grp + rr][128h + 8g .. +8]
 };
 
-template <int D, int TB>
-__device__ __forceinline__ void issue_tile(BTile<D, TB>& T, const __bf16* kbase, const __bf16* vbase,
+template <typename E, int D, int TB>
+__device__ __forceinline__ void issue_tile(BTile<D, TB>& T, const E* kbase, const E* vbase,
                                            int64_t block_elems, const int64_t (&phys)[TB],
                                            const bool (&valid)[TB], int g, int grp) {
   constexpr int NH = D / 128;
 #pragma unroll
   for (int b = 0; b < TB; ++b) {
     if (valid[b]) {
-      const __bf16* kb = kbase + phys[b] * block_elems;
-      const __bf16* vb = vbase + phys[b] * block_elems;
+      const E* kb = kbase + phys[b] * block_elems;
+      const E* vb = vbase + phys[b] * block_elems;
 #pragma unroll
       for (int rr = 0; rr < 4; ++rr)
 #pragma unroll
@@ -344,10 +384,12 @@ __device__ __forceinline__ int check_block_ids(const Params& P, int id, int s, c
 #define PA_D256_WAVES_PER_EU 2
 #endif
 
-template <int D, int NW, int TB, int PF, bool TRACE>
+template <typename T, int D, int NW, int TB, int PF, bool TRACE>
 __global__ __launch_bounds__(NW * 64)
 __attribute__((amdgpu_waves_per_eu(D == 128 ? PA_D128_WAVES_PER_EU : PA_D256_WAVES_PER_EU)))
-void pa_partition_bf16(Params P) {
+void pa_partition_h16(Params P) {
+  typedef typename H16<T>::x8 tx8;
+  typedef typename H16<T>::x4 tx4;
   extern __shared__ float smem[];
   constexpr int KK = D / 32;    // QK MFMAs per block (32 dims each)
   constexpr int NH = D / 128;   // 128-dim column groups
@@ -373,7 +415,7 @@ void pa_partition_bf16(Params P) {
   const int what = work_range(P, s, p, r);
   if (what == 0) return;
   if (what == 2) {
-    write_zeros<__bf16, D>(P, s, kvh, NW * 64);
+    write_zeros<T, D>(P, s, kvh, NW * 64);
     return;
   }
 
@@ -384,9 +426,9 @@ void pa_partition_bf16(Params P) {
 
   // B operand of the QK MFMA: lane holds q[head g][kk*32 + 8*grp .. +8],
   // either in registers or (QLDS) in LDS as [kk][lane], written once here.
-  bf16x8 qv[QLDS ? 1 : KK];
+  tx8 qv[QLDS ? 1 : KK];
   {
-    const __bf16* qrow = reinterpret_cast<const __bf16*>(P.q) + ((int64_t)s * P.H + kvh * P.G + g) * D;
+    const T* qrow = reinterpret_cast<const T*>(P.q) + ((int64_t)s * P.H + kvh * P.G + g) * D;
     if constexpr (QLDS) {
       for (int kk = w; kk < KK; kk += NW) {
         u32x4 x = {0u, 0u, 0u, 0u};
@@ -399,19 +441,19 @@ void pa_partition_bf16(Params P) {
       for (int kk = 0; kk < KK; ++kk) {
         u32x4 x = {0u, 0u, 0u, 0u};
         if (g < P.G) x = ld16(qrow + kk * 32 + grp * 8);
-        qv[kk] = __builtin_bit_cast(bf16x8, x);
+        qv[kk] = __builtin_bit_cast(tx8, x);
       }
     }
   }
-  auto q_operand = [&](int kk) -> bf16x8 {
-    if constexpr (QLDS) return __builtin_bit_cast(bf16x8, qlds[kk * 64 + lane]);
+  auto q_operand = [&](int kk) -> tx8 {
+    if constexpr (QLDS) return __builtin_bit_cast(tx8, qlds[kk * 64 + lane]);
     else return qv[kk];
   };
 
   const int64_t head_elems = (int64_t)kBS * D;     // one (block, kv head)
   const int64_t block_elems = head_elems * P.Hkv;  // one physical block
-  const __bf16* kbase = reinterpret_cast<const __bf16*>(P.k) + kvh * head_elems;
-  const __bf16* vbase = reinterpret_cast<const __bf16*>(P.v) + kvh * head_elems;
+  const T* kbase = reinterpret_cast<const T*>(P.k) + kvh * head_elems;
+  const T* vbase = reinterpret_cast<const T*>(P.v) + kvh * head_elems;
 
   float m = -INFINITY, lsum = 0.f;
   f32x4 acc[NACC];
@@ -435,7 +477,7 @@ void pa_partition_bf16(Params P) {
     }
   };
 
-  auto compute = [&](BTile<D, TB>& T, int t) {
+  auto compute = [&](BTile<D, TB>& tl, int t) {
     // K: registers -> swizzled LDS tile -> MFMA operand layout.
 #pragma unroll
     for (int b = 0; b < TB; ++b)
@@ -444,7 +486,7 @@ void pa_partition_bf16(Params P) {
 #pragma unroll
         for (int h = 0; h < NH; ++h) {
           const int row = 4 * grp + rr, c16 = 16 * h + g;
-          ktile[(b * 16 + row) * KCH + (c16 ^ row)] = T.k[b][rr][h];
+          ktile[(b * 16 + row) * KCH + (c16 ^ row)] = tl.k[b][rr][h];
         }
     f32x4 sc[TB];
 #pragma unroll
@@ -454,7 +496,7 @@ void pa_partition_bf16(Params P) {
       for (int kk = 0; kk < KK; ++kk) {
         const int c16 = 4 * kk + grp;
         const u32x4 kr = ktile[(b * 16 + g) * KCH + (c16 ^ g)];
-        sc[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kr), q_operand(kk), sc[b], 0, 0, 0);
+        sc[b] = H16<T>::mma32(__builtin_bit_cast(tx8, kr), q_operand(kk), sc[b]);
       }
     }
 
@@ -476,14 +518,14 @@ void pa_partition_bf16(Params P) {
     const float alpha = fast_exp2(m - mnew);
     m = mnew;
 
-    // P rounded to bf16; the exp-sum uses the same rounded values.
-    __bf16 pb[TB][4];
+    // P rounded to the cache's 16-bit type; the exp-sum uses the same rounded values.
+    T pb[TB][4];
     float ps = 0.f;
 #pragma unroll
     for (int b = 0; b < TB; ++b)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pb[b][i] = (__bf16)fast_exp2(x[b][i] - mnew);
+        pb[b][i] = (T)fast_exp2(x[b][i] - mnew);
         ps += (float)pb[b][i];
       }
     lsum = lsum * alpha + ps;
@@ -501,11 +543,11 @@ void pa_partition_bf16(Params P) {
         for (int rr = 0; rr < 4; ++rr)
           if (tok0 + b * kBS + 4 * grp + rr >= r.tok_end)
 #pragma unroll
-            for (int h = 0; h < NH; ++h) T.v[b][rr][h] = (u32x4){0u, 0u, 0u, 0u};
+            for (int h = 0; h < NH; ++h) tl.v[b][rr][h] = (u32x4){0u, 0u, 0u, 0u};
     }
 
     if constexpr (TB == 2) {
-      bf16x8 pv;
+      tx8 pv;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         pv[i] = pb[0][i];
@@ -518,25 +560,22 @@ void pa_partition_bf16(Params P) {
           const int c = j >> 1;
           u32x4 a;
           if (j & 1) {
-            a[0] = pack_hi(T.v[0][0][h][c], T.v[0][1][h][c]);
-            a[1] = pack_hi(T.v[0][2][h][c], T.v[0][3][h][c]);
-            a[2] = pack_hi(T.v[1][0][h][c], T.v[1][1][h][c]);
-            a[3] = pack_hi(T.v[1][2][h][c], T.v[1][3][h][c]);
+            a[0] = pack_hi(tl.v[0][0][h][c], tl.v[0][1][h][c]);
+            a[1] = pack_hi(tl.v[0][2][h][c], tl.v[0][3][h][c]);
+            a[2] = pack_hi(tl.v[1][0][h][c], tl.v[1][1][h][c]);
+            a[3] = pack_hi(tl.v[1][2][h][c], tl.v[1][3][h][c]);
           } else {
-            a[0] = pack_lo(T.v[0][0][h][c], T.v[0][1][h][c]);
-            a[1] = pack_lo(T.v[0][2][h][c], T.v[0][3][h][c]);
-            a[2] = pack_lo(T.v[1][0][h][c], T.v[1][1][h][c]);
-            a[3] = pack_lo(T.v[1][2][h][c], T.v[1][3][h][c]);
+            a[0] = pack_lo(tl.v[0][0][h][c], tl.v[0][1][h][c]);
+            a[1] = pack_lo(tl.v[0][2][h][c], tl.v[0][3][h][c]);
+            a[2] = pack_lo(tl.v[1][0][h][c], tl.v[1][1][h][c]);
+            a[3] = pack_lo(tl.v[1][2][h][c], tl.v[1][3][h][c]);
           }
-          acc[h * 8 + j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), pv,
-                                                                   acc[h * 8 + j], 0, 0, 0);
+          acc[h * 8 + j] = H16<T>::mma32(__builtin_bit_cast(tx8, a), pv, acc[h * 8 + j]);
         }
     } else {
-      typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-      bf16x4 pv4;
+      tx4 pv4;
 #pragma unroll
       for (int i = 0; i < 4; ++i) pv4[i] = pb[0][i];
-      const i16x4 pvi = __builtin_bit_cast(i16x4, pv4);
 #pragma unroll
       for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -544,14 +583,13 @@ void pa_partition_bf16(Params P) {
           const int c = j >> 1;
           u32x2 a;
           if (j & 1) {
-            a[0] = pack_hi(T.v[0][0][h][c], T.v[0][1][h][c]);
-            a[1] = pack_hi(T.v[0][2][h][c], T.v[0][3][h][c]);
+            a[0] = pack_hi(tl.v[0][0][h][c], tl.v[0][1][h][c]);
+            a[1] = pack_hi(tl.v[0][2][h][c], tl.v[0][3][h][c]);
           } else {
-            a[0] = pack_lo(T.v[0][0][h][c], T.v[0][1][h][c]);
-            a[1] = pack_lo(T.v[0][2][h][c], T.v[0][3][h][c]);
+            a[0] = pack_lo(tl.v[0][0][h][c], tl.v[0][1][h][c]);
+            a[1] = pack_lo(tl.v[0][2][h][c], tl.v[0][3][h][c]);
           }
-          acc[h * 8 + j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4, a), pvi,
-                                                                     acc[h * 8 + j], 0, 0, 0);
+          acc[h * 8 + j] = H16<T>::mma16(__builtin_bit_cast(tx4, a), pv4, acc[h * 8 + j]);
         }
     }
   };
@@ -561,21 +599,21 @@ void pa_partition_bf16(Params P) {
     int64_t phys[TB];
     bool valid[TB];
     tile_ids(t0, phys, valid);
-    issue_tile<D, TB>(A, kbase, vbase, block_elems, phys, valid, g, grp);
+    issue_tile<T, D, TB>(A, kbase, vbase, block_elems, phys, valid, g, grp);
     if constexpr (PF) {
       // Two register stages, unrolled so that A and B swap roles without copies.
       for (int t = t0;;) {
         const int t1 = t + dt;
         if (t1 < ntiles) {
           tile_ids(t1, phys, valid);
-          issue_tile<D, TB>(B, kbase, vbase, block_elems, phys, valid, g, grp);
+          issue_tile<T, D, TB>(B, kbase, vbase, block_elems, phys, valid, g, grp);
         }
         compute(A, t);
         if (t1 >= ntiles) break;
         const int t2 = t1 + dt;
         if (t2 < ntiles) {
           tile_ids(t2, phys, valid);
-          issue_tile<D, TB>(A, kbase, vbase, block_elems, phys, valid, g, grp);
+          issue_tile<T, D, TB>(A, kbase, vbase, block_elems, phys, valid, g, grp);
         }
         compute(B, t1);
         if (t2 >= ntiles) break;
@@ -587,14 +625,14 @@ void pa_partition_bf16(Params P) {
         t += dt;
         if (t >= ntiles) break;
         tile_ids(t, phys, valid);
-        issue_tile<D, TB>(A, kbase, vbase, block_elems, phys, valid, g, grp);
+        issue_tile<T, D, TB>(A, kbase, vbase, block_elems, phys, valid, g, grp);
       }
     }
   }
 
   lsum = group_sum(lsum);
   // acc[h*8 + j][i] holds dim 128h + 32*grp + 8i + j.
-  merge_and_write<__bf16, D, NACC, NW>(P, r, s, kvh, p, w, lane, acc, m, lsum, smem, [&](int a, int i) {
+  merge_and_write<T, D, NACC, NW>(P, r, s, kvh, p, w, lane, acc, m, lsum, smem, [&](int a, int i) {
     const int h = a >> 3, j = a & 7;
     return 128 * h + 32 * grp + 8 * i + j;
   });
@@ -848,7 +886,7 @@ int check_shape(const pa_shape* sh) {
   if (sh->num_heads / sh->num_kv_heads > 16) return PA_EUNSUPPORTED;
   if (sh->head_dim != 128 && sh->head_dim != 256) return PA_EUNSUPPORTED;
   if (sh->block_size != kBS) return PA_EUNSUPPORTED;
-  if (sh->dtype != PA_F32 && sh->dtype != PA_BF16) return PA_EUNSUPPORTED;
+  if (sh->dtype != PA_F32 && sh->dtype != PA_BF16 && sh->dtype != PA_F16) return PA_EUNSUPPORTED;
   if (sh->max_blocks_per_seq > (1 << 26)) return PA_EUNSUPPORTED;  // keeps token counts in int32
   return PA_OK;
 }
@@ -887,16 +925,16 @@ size_t merge_bytes(int nw, int D, int G) {
   return ((size_t)2 * nw * 16 + (size_t)nw * G * (D + 4)) * sizeof(float);
 }
 
-template <int D, int NW, int TB>
-hipError_t launch_bf16(const Params& P, bool trace, dim3 grid, hipStream_t stream) {
+template <typename T, int D, int NW, int TB>
+hipError_t launch_h16(const Params& P, bool trace, dim3 grid, hipStream_t stream) {
   constexpr int NACC = (D / 128) * 8;
   constexpr bool QLDS = (D == 128) ? PA_D128_Q_LDS : PA_D256_Q_LDS;
   const size_t head = (size_t)2 * NW * 16 * sizeof(float);
   const size_t qarea = QLDS ? (size_t)(D / 32) * 64 * 16 : 0;
-  const size_t ktiles = (size_t)NW * TB * 16 * D * sizeof(__bf16);
+  const size_t ktiles = (size_t)NW * TB * 16 * D * sizeof(T);
   const size_t smem = head + std::max(qarea + ktiles, merge_bytes(NW, D, P.G) - head);
-  auto kern = trace ? pa_partition_bf16<D, NW, TB, PA_PREFETCH, true>
-                    : pa_partition_bf16<D, NW, TB, PA_PREFETCH, false>;
+  auto kern = trace ? pa_partition_h16<T, D, NW, TB, PA_PREFETCH, true>
+                    : pa_partition_h16<T, D, NW, TB, PA_PREFETCH, false>;
   if (smem > 65536) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
@@ -919,8 +957,12 @@ hipError_t launch_partitions(const Params& P, int D, int dtype, bool trace, hipS
   const dim3 grid((unsigned)((int64_t)P.S * P.Hkv * pgrid));
   if (grid.x == 0) return hipSuccess;
   if (dtype == PA_BF16) {
-    if (D == 128) return launch_bf16<128, PA_BF16_D128_NW, PA_BF16_D128_TB>(P, trace, grid, stream);
-    return launch_bf16<256, PA_BF16_D256_NW, PA_BF16_D256_TB>(P, trace, grid, stream);
+    if (D == 128) return launch_h16<__bf16, 128, PA_BF16_D128_NW, PA_BF16_D128_TB>(P, trace, grid, stream);
+    return launch_h16<__bf16, 256, PA_BF16_D256_NW, PA_BF16_D256_TB>(P, trace, grid, stream);
+  }
+  if (dtype == PA_F16) {
+    if (D == 128) return launch_h16<_Float16, 128, PA_BF16_D128_NW, PA_BF16_D128_TB>(P, trace, grid, stream);
+    return launch_h16<_Float16, 256, PA_BF16_D256_NW, PA_BF16_D256_TB>(P, trace, grid, stream);
   }
   if (D == 128) return launch_f32<128>(P, trace, grid, stream);
   return launch_f32<256>(P, trace, grid, stream);
@@ -952,7 +994,9 @@ hipError_t launch_reduce_t(const ReduceParams& R, hipStream_t stream) {
 }
 
 hipError_t launch_reduce(const ReduceParams& R, int dtype, hipStream_t stream) {
-  return dtype == PA_BF16 ? launch_reduce_t<__bf16>(R, stream) : launch_reduce_t<float>(R, stream);
+  if (dtype == PA_BF16) return launch_reduce_t<__bf16>(R, stream);
+  if (dtype == PA_F16) return launch_reduce_t<_Float16>(R, stream);
+  return launch_reduce_t<float>(R, stream);
 }
 
 Params make_params(void* out, const void* q, const void* k, const void* v, const int32_t* bt,

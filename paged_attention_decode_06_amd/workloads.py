@@ -46,7 +46,7 @@ class DecodeConfig:
     num_heads: int
     num_kv_heads: int
     head_dim: int
-    dtype: str                 # "f32" or "bf16"
+    dtype: str                 # "f32", "bf16" or "f16"
     lengths: tuple             # ("fixed", L) | ("uniform", lo, hi) | ("loguniform", lo, hi)
     pool_blocks: int | None = None   # fixed pool size (tiny config); None = exactly what is used
     k_outlier_frac: float = 0.0      # fraction of K scalars multiplied by k_outlier_mult
@@ -66,12 +66,14 @@ CONFIGS = {
     4: DecodeConfig("batch64-logU512-65536-bf16", 64, 16, 2, 128, "bf16", ("loguniform", 512, 65536)),
     5: DecodeConfig("batch256-U1024-32768-d256-bf16", 256, 16, 2, 256, "bf16", ("uniform", 1024, 32768),
                     k_outlier_frac=0.01, k_outlier_mult=20.0),
+    # fp16-cache variant of the 100K-token decode (the model's other 16-bit type)
+    6: DecodeConfig("ctx100K-f16", 1, 16, 2, 128, "f16", ("fixed", 100000)),
 }
 
 
 @dataclass
 class DecodeInputs:
-    """Host-side inputs. bf16 arrays are stored as uint16 bit patterns."""
+    """Host-side inputs. bf16 arrays are stored as uint16 bit patterns, f16 as float16."""
     cfg: DecodeConfig
     seed: int
     seq_lens: np.ndarray        # int32 [S]
@@ -133,6 +135,8 @@ def _fill_normal(out_flat: np.ndarray, seed: int, purpose: int, dtype: str,
             vals[mask] *= np.float32(outlier_mult)
         if dtype == "f32":
             out_flat[lo:hi] = vals
+        elif dtype == "f16":
+            out_flat[lo:hi] = vals.astype(np.float16)   # round to nearest even
         else:
             out_flat[lo:hi] = f32_to_bf16_bits(vals)
 
@@ -215,7 +219,7 @@ def make_inputs(cfg: DecodeConfig | int, seed: int | None = None, *, seq_lens=No
     pb = pool_blocks if pool_blocks is not None else cfg.pool_blocks
     tables, nb = build_tables(lens, trng, pb, max_blocks_per_seq)
     S, H, Hkv, D = cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim
-    store = np.float32 if cfg.dtype == "f32" else np.uint16
+    store = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[cfg.dtype]
     nb_alloc = nb + (1 if poison else 0)
 
     q = np.empty((S, H, D), dtype=store)
@@ -236,6 +240,8 @@ def _poison(lens, tables, k, v, poison_block, dtype) -> None:
     """Fill every slot no context reaches with NaN (V) and +Inf/NaN (K)."""
     if dtype == "f32":
         nan, inf = np.float32(np.nan), np.float32(np.inf)
+    elif dtype == "f16":
+        nan, inf = np.float16(np.nan), np.float16(np.inf)
     else:
         nan, inf = np.uint16(0x7FC0), np.uint16(0x7F80)
     used = np.zeros(k.shape[0], dtype=bool)

@@ -49,6 +49,7 @@ def test_header_constants_match_binding():
 def test_valid_args_pass(lib):
     assert check(lib, shape()) == L.PA_OK
     assert check(lib, shape(dtype=L.PA_F32, head_dim=256, num_heads=2, num_kv_heads=1)) == L.PA_OK
+    assert check(lib, shape(dtype=L.PA_F16)) == L.PA_OK
     # single pass needs no partial buffers
     assert check(lib, shape(), L.MODE_V1, es=None, ml=None, to=None) == L.PA_OK
 

@@ -14,7 +14,7 @@ from paged_attention_decode_06_amd import workloads as W
 
 pytestmark = pytest.mark.gpu
 
-TOL = {"f32": 1e-3, "bf16": 2e-2}
+TOL = {"f32": 1e-3, "bf16": 2e-2, "f16": 1e-2}
 MODES = ("auto", "v1", "v2")
 # Table widths: the natural one, and 4096 blocks, which gives 128 partitions
 # per sequence and so exercises the one-partition-per-wave launch layout.
@@ -106,15 +106,25 @@ def test_config_parity(dev, num):
     assert np.isfinite(got).all()
 
 
+def test_long_context_f16(dev):
+    """The 100K-token shape with an fp16 cache (fp16 variant of the path)."""
+    cfg = W.DecodeConfig("ctx100K-f16", 1, 16, 2, 128, "f16", ("fixed", 100000))
+    x = W.make_inputs(cfg, seed=1103)
+    say("100K-token context, fp16 cache")
+    out, _ = run(x, dev, "auto")
+    assert np.isfinite(assert_close(x, out, label="auto")).all()
+
+
 # ---------------------------------------------------------------- paths agree
 MIXED = [1, 37, 512, 513, 5000, 8192, 8193, 20000]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("width", WIDTHS)
 @pytest.mark.parametrize("D", [128, 256])
 @pytest.mark.parametrize("mode", MODES)
-def test_modes_vs_oracle(dev, D, mode, width):
-    cfg = W.DecodeConfig(f"mixed-d{D}", len(MIXED), 16, 2, D, "bf16", ("custom",))
+def test_modes_vs_oracle(dev, D, mode, width, dtype):
+    cfg = W.DecodeConfig(f"mixed-{dtype}-d{D}", len(MIXED), 16, 2, D, dtype, ("custom",))
     x = W.make_inputs(cfg, seed=11, seq_lens=MIXED, max_blocks_per_seq=width)
     say(f"mode {mode} D={D} lens={MIXED} table width={x.max_blocks_per_seq}")
     out, _ = run(x, dev, mode)
@@ -136,7 +146,8 @@ def test_v1_and_v2_agree(dev):
 
 
 @pytest.mark.parametrize("dtype,D,H,Hkv", [("bf16", 128, 32, 2), ("bf16", 256, 4, 4), ("f32", 256, 3, 1),
-                                           ("f32", 128, 16, 2), ("bf16", 128, 5, 1)])
+                                           ("f32", 128, 16, 2), ("bf16", 128, 5, 1), ("f16", 128, 16, 2),
+                                           ("f16", 256, 8, 1)])
 @pytest.mark.parametrize("mode", MODES)
 def test_group_sizes(dev, dtype, D, H, Hkv, mode):
     lens = [3, 600, 9000]
@@ -151,7 +162,7 @@ def test_group_sizes(dev, dtype, D, H, Hkv, mode):
 EDGE = [1, 15, 16, 17, 37, 511, 512, 513, 8191, 8192, 8193, 16384]
 
 
-@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 256), ("f32", 128)])
+@pytest.mark.parametrize("dtype,D", [("bf16", 128), ("bf16", 256), ("f32", 128), ("f16", 128), ("f16", 256)])
 @pytest.mark.parametrize("mode", MODES)
 def test_edge_lengths(dev, dtype, D, mode):
     cfg = W.DecodeConfig(f"edge-{dtype}-d{D}", len(EDGE), 16, 2, D, dtype, ("custom",))
@@ -181,7 +192,7 @@ def test_empty_batch(dev):
     assert out.numel() == 0
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 @pytest.mark.parametrize("width", [600, 4096])
 @pytest.mark.parametrize("mode", MODES)
 def test_poison_outside_contexts_never_reaches_output(dev, dtype, mode, width):
@@ -217,7 +228,7 @@ def test_runs_are_bitwise_deterministic(dev):
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 def test_single_token_returns_v_exactly(dev, dtype):
     cfg = W.DecodeConfig("one", 3, 16, 2, 128, dtype, ("custom",))
     x = W.make_inputs(cfg, seed=19, seq_lens=[1, 1, 1])
@@ -307,7 +318,7 @@ REDUCE_SHAPES = [(3, 4, 128), (64, 16, 128), (128, 16, 128), (128, 16, 256)]
 
 
 @pytest.mark.parametrize("S,H,D", REDUCE_SHAPES)
-@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
 def test_reduce_fed_with_oracle_partials(dev, dtype, S, H, D):
     rng = np.random.default_rng(24)
     MB = 100                               # Pmax = ceil(100*16/512) = 4
@@ -320,14 +331,15 @@ def test_reduce_fed_with_oracle_partials(dev, dtype, S, H, D):
         n = oracle.num_partitions(int(lens[s]))
         for h in range(H):
             want[s, h] = oracle.lse_combine(m[s, h, :n], l[s, h, :n], o[s, h, :n])
-    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
+    code = {"bf16": pa.PA_BF16, "f16": pa.PA_F16, "f32": pa.PA_F32}[dtype]
     out = torch.full((S, H, D), float("nan"), dtype=tdt, device=dev)
     to_t = lambda a: torch.from_numpy(a.astype(np.float32)).to(dev)
-    sh = pa.PaShape(S, H, 1, D, 16, MB, 10, pa.PA_BF16 if dtype == "bf16" else pa.PA_F32)
+    sh = pa.PaShape(S, H, 1, D, 16, MB, 10, code)
     say(f"reduce from oracle partials {dtype} S={S} H={H} D={D}")
     pa.pa_lse_reduce(out, to_t(l), to_t(m), to_t(o), torch.from_numpy(lens).to(dev), sh, pa.MODE_V2)
     torch.cuda.synchronize(dev)
-    assert max_err(W.from_device(out), want) <= (2e-2 if dtype == "bf16" else 1e-5)
+    assert max_err(W.from_device(out), want) <= {"bf16": 2e-2, "f16": 5e-3, "f32": 1e-5}[dtype]
 
 
 @pytest.mark.parametrize("width", WIDTHS)

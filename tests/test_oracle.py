@@ -257,6 +257,12 @@ def test_unreferenced_and_tail_slots_never_read():
     assert np.isfinite(out).all()
 
 
+def test_widen_f16_values():
+    v = np.array([1.0, -2.5, 65504.0, 2.0 ** -24, np.inf], dtype=np.float16)
+    w = oracle.widen(v, "f16")
+    assert w.tolist()[:4] == [1.0, -2.5, 65504.0, 2.0 ** -24] and np.isinf(w[4])
+
+
 def test_widen_bf16_bit_patterns():
     bits = np.array([0x3F80, 0xC000, 0x7F80, 0x0001, 0x3E80], dtype=np.uint16)
     w = oracle.widen(bits, "bf16")

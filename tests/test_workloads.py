@@ -18,6 +18,18 @@ def test_bf16_rounding_nearest_even():
     assert np.array_equal(W.bf16_bits_to_f32(b[:3]), np.array([1.0, 1.0, 1 + 2**-6], np.float32))
 
 
+def test_f16_generation_rounds_like_numpy():
+    cfg = W.DecodeConfig("t16", 2, 4, 2, 128, "f16", ("fixed", 40))
+    x = W.make_inputs(cfg, seed=3)
+    assert x.k_cache.dtype == np.float16 and x.q.dtype == np.float16
+    # the same draws in fp32, rounded by NumPy, give the stored values
+    ref = np.random.Generator(np.random.PCG64(np.random.SeedSequence(3, spawn_key=(1, 0)))).standard_normal(
+        x.q.size, dtype=np.float32).astype(np.float16)
+    assert np.array_equal(x.q.reshape(-1), ref)
+    p = W.make_inputs(cfg, seed=3, poison=True)
+    assert np.isnan(p.v_cache[p.extra["poison_block"]]).all()
+
+
 def test_tiny_config_shape():
     x = W.make_inputs(1)
     assert x.seq_lens.tolist() == [37]
