@@ -36,7 +36,9 @@
  * synchronises; `shape` is a host pointer read during the call only.
  * Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  * stream). Calls hold no state and may run concurrently when their outputs
- * and partial buffers are disjoint.
+ * and partial buffers are disjoint. Results are bitwise reproducible for the
+ * same entry point and shape (the launch shape, and so the rounding order,
+ * depends on the mode and the sizes only).
  *
  * Errors: a negative status is returned and nothing is launched when an
  * argument is invalid; PA_EHIP reports a failed launch. Data errors are

@@ -952,16 +952,33 @@ hipError_t launch_f32(const Params& P, bool trace, dim3 grid, hipStream_t stream
   return hipGetLastError();
 }
 
+// Launch shape of the 16-bit kernel at head_dim 128, chosen from sizes alone
+// (no device data is read on the host):
+//   single-pass only (mode V1, or a table no wider than the V1 threshold):
+//     few long workgroups -> 8 waves, two-block tiles;
+//   small grids (<= kSmallGrid workgroups, about 4 per CU): one-block tiles,
+//     whose lower register count keeps 4 waves per SIMD resident;
+//   otherwise 4 waves, two-block tiles.
+constexpr int64_t kSmallGrid = 1024;
+
+template <typename T>
+hipError_t launch_h16_d128(const Params& P, bool trace, dim3 grid, hipStream_t stream) {
+  const bool single_pass = P.mode == PA_MODE_V1 || (int64_t)P.MB * kBS <= kThresh;
+  if (single_pass) return launch_h16<T, 128, 8, 2>(P, trace, grid, stream);
+  if ((int64_t)grid.x <= kSmallGrid) return launch_h16<T, 128, 4, 1>(P, trace, grid, stream);
+  return launch_h16<T, 128, PA_BF16_D128_NW, PA_BF16_D128_TB>(P, trace, grid, stream);
+}
+
 hipError_t launch_partitions(const Params& P, int D, int dtype, bool trace, hipStream_t stream) {
   const int64_t pgrid = (P.mode == PA_MODE_V1) ? 1 : P.Pmax;
   const dim3 grid((unsigned)((int64_t)P.S * P.Hkv * pgrid));
   if (grid.x == 0) return hipSuccess;
   if (dtype == PA_BF16) {
-    if (D == 128) return launch_h16<__bf16, 128, PA_BF16_D128_NW, PA_BF16_D128_TB>(P, trace, grid, stream);
+    if (D == 128) return launch_h16_d128<__bf16>(P, trace, grid, stream);
     return launch_h16<__bf16, 256, PA_BF16_D256_NW, PA_BF16_D256_TB>(P, trace, grid, stream);
   }
   if (dtype == PA_F16) {
-    if (D == 128) return launch_h16<_Float16, 128, PA_BF16_D128_NW, PA_BF16_D128_TB>(P, trace, grid, stream);
+    if (D == 128) return launch_h16_d128<_Float16>(P, trace, grid, stream);
     return launch_h16<_Float16, 256, PA_BF16_D256_NW, PA_BF16_D256_TB>(P, trace, grid, stream);
   }
   if (D == 128) return launch_f32<128>(P, trace, grid, stream);
