@@ -144,6 +144,21 @@ int pa_decode_partitions_debug(void* out, const void* q, const void* k_cache, co
                                float* max_logits, float* tmp_out, int mode,
                                int32_t* gather_trace, int32_t* err_flag, void* stream);
 
+/* Measurement forms of pa_decode_partitions and pa_lse_reduce: the kernel is
+ * launched with start_event recorded as it begins and stop_event as it ends
+ * (hipEvent_t handles created by the caller; either may be NULL), so the
+ * pair times that kernel alone, on `stream`. When there is nothing to launch
+ * (an empty batch, or PA_MODE_V1 for the reduce) both events are recorded
+ * back to back on `stream`, so the pair still completes. */
+int pa_decode_partitions_timed(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               const pa_shape* shape, float scale, float* exp_sums,
+                               float* max_logits, float* tmp_out, int mode, void* start_event,
+                               void* stop_event, void* stream);
+int pa_lse_reduce_timed(void* out, const float* exp_sums, const float* max_logits, const float* tmp_out,
+                        const int32_t* seq_lens, const pa_shape* shape, int mode, void* start_event,
+                        void* stop_event, void* stream);
+
 /* Pmax = ceil(max_blocks_per_seq * 16 / 512), or a negative status. */
 int64_t pa_max_partitions(const pa_shape* shape);
 

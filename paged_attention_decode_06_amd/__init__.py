@@ -5,7 +5,8 @@ this package is its thin ctypes binding plus the seeded input generators
 (`workloads`). Build the library with `python -m paged_attention_decode_06_amd._build`.
 """
 from ._lib import (  # noqa: F401
-    BLOCK_SIZE, PARTITION_SIZE, V2_THRESHOLD, MODE_AUTO, MODE_V1, MODE_V2, PA_F32, PA_BF16, PA_F16,
+    BLOCK_SIZE, HipEvents, PARTITION_SIZE, V2_THRESHOLD, MODE_AUTO, MODE_V1, MODE_V2, PA_F32, PA_BF16, PA_F16,
     PaError, PaShape, alloc_partials, load, make_shape, max_partitions, pa_decode, pa_decode_partitions,
-    pa_decode_partitions_debug, pa_decode_v1, pa_decode_v2, pa_lse_reduce, status_string,
+    pa_decode_partitions_debug, pa_decode_partitions_timed, pa_decode_v1, pa_decode_v2, pa_lse_reduce,
+    pa_lse_reduce_timed, status_string,
 )

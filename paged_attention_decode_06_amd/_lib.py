@@ -51,6 +51,9 @@ _SIGS = {
     "pa_lse_reduce": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_int, _P]),
     "pa_decode_partitions_debug": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_float,
                                                   _P, _P, _P, ctypes.c_int, _P, _P, _P]),
+    "pa_decode_partitions_timed": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_float,
+                                                  _P, _P, _P, ctypes.c_int, _P, _P, _P]),
+    "pa_lse_reduce_timed": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_int, _P, _P, _P]),
     "pa_max_partitions": (ctypes.c_int64, [ctypes.POINTER(PaShape)]),
     "pa_partials_elems": (ctypes.c_int64, [ctypes.POINTER(PaShape), ctypes.c_int]),
     "pa_check_args": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), _P, _P, _P, ctypes.c_int]),
@@ -221,3 +224,59 @@ def pa_lse_reduce(out, exp_sums, max_logits, tmp_out, seq_lens, shape: PaShape, 
     _call("pa_lse_reduce", load().pa_lse_reduce(_ptr(out), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out),
                                                 _ptr(seq_lens), ctypes.byref(shape), int(mode),
                                                 _stream(stream, out.device)))
+
+
+def pa_decode_partitions_timed(out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits,
+                               tmp_out, mode, start_event, stop_event, stream=None):
+    """Phase 1 with raw hipEvent_t handles (ints) recorded around the kernel itself."""
+    _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens, (exp_sums, max_logits, tmp_out))
+    sh = make_shape(q, k_cache, block_tables)
+    _call("pa_decode_partitions_timed", load().pa_decode_partitions_timed(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
+        ctypes.byref(sh), float(scale), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), int(mode),
+        ctypes.c_void_p(start_event), ctypes.c_void_p(stop_event), _stream(stream, q.device)))
+
+
+def pa_lse_reduce_timed(out, exp_sums, max_logits, tmp_out, seq_lens, shape: PaShape, mode, start_event,
+                        stop_event, stream=None):
+    """Phase 2 with raw hipEvent_t handles (ints) recorded around the kernel itself."""
+    _check_tensors(out, None, None, None, None, seq_lens, (exp_sums, max_logits, tmp_out))
+    _call("pa_lse_reduce_timed", load().pa_lse_reduce_timed(
+        _ptr(out), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), _ptr(seq_lens), ctypes.byref(shape),
+        int(mode), ctypes.c_void_p(start_event), ctypes.c_void_p(stop_event), _stream(stream, out.device)))
+
+
+class HipEvents:
+    """Raw hipEvent_t handles for the *_timed entry points.
+
+    The handles come from the HIP runtime this process already has mapped (the
+    one the library itself is linked against), opened without loading a
+    second copy. They are freed by close().
+    """
+
+    def __init__(self):
+        load()  # maps the runtime the library is linked against
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.made = []
+
+    def new(self) -> int:
+        h = self.ct.c_void_p()
+        if self.hip.hipEventCreate(self.ct.byref(h)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        self.made.append(h.value)
+        return h.value
+
+    def ms(self, a: int, b: int) -> float:
+        out = self.ct.c_float()
+        if self.hip.hipEventElapsedTime(self.ct.byref(out), self.ct.c_void_p(a), self.ct.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(out.value)
+
+    def close(self):
+        for h in self.made:
+            self.hip.hipEventDestroy(self.ct.c_void_p(h))
+        self.made = []

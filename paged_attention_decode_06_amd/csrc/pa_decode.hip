@@ -28,6 +28,7 @@
 // table width and out-of-range block ids are read as block 0 (both reported
 // through the optional error word).
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -763,6 +764,9 @@ __global__ __launch_bounds__(NW * 64) void pa_partition_f32(Params P) {
 // rescale the running sums to the new max. The host picks CW: full rows (one
 // coalesced 1 KB row per wave at D = 256) when there are enough (sequence,
 // head) rows to fill the GPU, narrow slices (more workgroups) otherwise.
+// With SPEC (small partial sets, where the kernel is latency-bound) the first
+// group's loads go out before the sequence length arrives, bounded by Pmax,
+// and entries past the sequence's partition count are masked afterwards.
 // Summation order is fixed (bitwise deterministic).
 struct ReduceParams {
   void* out;
@@ -773,7 +777,7 @@ struct ReduceParams {
   int S, H, MB, Pmax, mode, D;
 };
 
-template <typename T, int CW>
+template <typename T, int CW, bool SPEC>
 __global__ __launch_bounds__(kReduceThreads) void pa_lse_reduce_kernel(ReduceParams R) {
   constexpr int F4 = CW / 4;                 // float4 per slice
   constexpr int PG = kReduceThreads / F4;    // partition groups
@@ -785,25 +789,17 @@ __global__ __launch_bounds__(kReduceThreads) void pa_lse_reduce_kernel(ReducePar
   const int sh = blockIdx.x / nchunk;
   const int s = sh / R.H;
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
-  int L = R.sl[s];
-  if (L > R.MB * kBS) L = R.MB * kBS;
-  if (L < 0) L = 0;
-  if (R.mode == PA_MODE_AUTO && L <= kThresh) return;
-  const int np = (L + kPart - 1) / kPart;
   const float* ml = R.max_logits + (int64_t)sh * R.Pmax;
   const float* es = R.exp_sums + (int64_t)sh * R.Pmax;
   const float* to = R.tmp_out + (int64_t)sh * R.Pmax * R.D + dc * CW;
   const int f4 = t % F4, pg = t / F4;
-
-  float M = -INFINITY, ctot = 0.f;
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  for (int base = 0; base < np; base += PG * NU) {
-    float mv[NU], ev[NU];
-    f32x4 v[NU];
+  float mv[NU], ev[NU];
+  f32x4 v[NU];
+  auto load_group = [&](int base, int limit) {
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
       const int pp = base + pg + PG * u;
-      if (pp < np) {
+      if (pp < limit) {
         mv[u] = ml[pp];
         ev[u] = es[pp];
         v[u] = *reinterpret_cast<const f32x4*>(to + (int64_t)pp * R.D + 4 * f4);
@@ -812,6 +808,29 @@ __global__ __launch_bounds__(kReduceThreads) void pa_lse_reduce_kernel(ReducePar
         ev[u] = 0.f;
         v[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
       }
+    }
+  };
+  if constexpr (SPEC) load_group(0, R.Pmax);
+  int L = R.sl[s];
+  if (L > R.MB * kBS) L = R.MB * kBS;
+  if (L < 0) L = 0;
+  if (R.mode == PA_MODE_AUTO && L <= kThresh) return;
+  const int np = (L + kPart - 1) / kPart;
+
+  float M = -INFINITY, ctot = 0.f;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  for (int base = 0; base < np; base += PG * NU) {
+    if (SPEC && base == 0) {
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        if (pg + PG * u >= np) {
+          mv[u] = -INFINITY;
+          ev[u] = 0.f;
+          v[u] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        }
+      }
+    } else {
+      load_group(base, np);
     }
     float cm = mv[0];
 #pragma unroll
@@ -869,6 +888,12 @@ __global__ __launch_bounds__(kReduceThreads) void pa_lse_reduce_kernel(ReducePar
 #ifndef PA_BF16_D256_TB
 #define PA_BF16_D256_TB 1
 #endif
+#ifndef PA_V1_D128_NW
+#define PA_V1_D128_NW 8
+#endif
+#ifndef PA_V1_D128_TB
+#define PA_V1_D128_TB 2
+#endif
 #ifndef PA_PREFETCH
 #define PA_PREFETCH 0
 #endif
@@ -925,8 +950,32 @@ size_t merge_bytes(int nw, int D, int G) {
   return ((size_t)2 * nw * 16 + (size_t)nw * G * (D + 4)) * sizeof(float);
 }
 
+// Where a kernel goes: the stream, and optionally a pair of events recorded
+// at the start and the end of that kernel alone (measurement entry points).
+struct Launch {
+  hipStream_t stream;
+  hipEvent_t start, stop;
+};
+
+template <typename K, typename A>
+hipError_t launch(K kern, dim3 grid, dim3 block, size_t smem, const Launch& L, const A& arg) {
+  if (L.start || L.stop)
+    hipExtLaunchKernelGGL(kern, grid, block, (uint32_t)smem, L.stream, L.start, L.stop, 0, arg);
+  else
+    hipLaunchKernelGGL(kern, grid, block, smem, L.stream, arg);
+  return hipGetLastError();
+}
+
+// When there is nothing to launch, a timed call still records its events,
+// back to back, so the caller's pair always completes and reads ~0.
+hipError_t nothing_launched(const Launch& L) {
+  if (L.start && hipEventRecord(L.start, L.stream) != hipSuccess) return hipGetLastError();
+  if (L.stop && hipEventRecord(L.stop, L.stream) != hipSuccess) return hipGetLastError();
+  return hipSuccess;
+}
+
 template <typename T, int D, int NW, int TB>
-hipError_t launch_h16(const Params& P, bool trace, dim3 grid, hipStream_t stream) {
+hipError_t launch_h16(const Params& P, bool trace, dim3 grid, const Launch& L) {
   constexpr int NACC = (D / 128) * 8;
   constexpr bool QLDS = (D == 128) ? PA_D128_Q_LDS : PA_D256_Q_LDS;
   const size_t head = (size_t)2 * NW * 16 * sizeof(float);
@@ -940,16 +989,14 @@ hipError_t launch_h16(const Params& P, bool trace, dim3 grid, hipStream_t stream
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
   }
-  hipLaunchKernelGGL(kern, grid, dim3(NW * 64), smem, stream, P);
-  return hipGetLastError();
+  return launch(kern, grid, dim3(NW * 64), smem, L, P);
 }
 
 template <int D>
-hipError_t launch_f32(const Params& P, bool trace, dim3 grid, hipStream_t stream) {
+hipError_t launch_f32(const Params& P, bool trace, dim3 grid, const Launch& L) {
   const size_t smem = merge_bytes(kNW, D, P.G);
   auto kern = trace ? pa_partition_f32<D, kNW, true> : pa_partition_f32<D, kNW, false>;
-  hipLaunchKernelGGL(kern, grid, dim3(kNW * 64), smem, stream, P);
-  return hipGetLastError();
+  return launch(kern, grid, dim3(kNW * 64), smem, L, P);
 }
 
 // Launch shape of the 16-bit kernel at head_dim 128, chosen from sizes alone
@@ -962,17 +1009,17 @@ hipError_t launch_f32(const Params& P, bool trace, dim3 grid, hipStream_t stream
 constexpr int64_t kSmallGrid = 1024;
 
 template <typename T>
-hipError_t launch_h16_d128(const Params& P, bool trace, dim3 grid, hipStream_t stream) {
-  const bool single_pass = P.mode == PA_MODE_V1 || (int64_t)P.MB * kBS <= kThresh;
-  if (single_pass) return launch_h16<T, 128, 8, 2>(P, trace, grid, stream);
-  if ((int64_t)grid.x <= kSmallGrid) return launch_h16<T, 128, 4, 1>(P, trace, grid, stream);
-  return launch_h16<T, 128, PA_BF16_D128_NW, PA_BF16_D128_TB>(P, trace, grid, stream);
+hipError_t launch_h16_d128(const Params& P, bool trace, dim3 grid, const Launch& L) {
+  const bool single_pass = P.mode == PA_MODE_V1 || (P.mode == PA_MODE_AUTO && (int64_t)P.MB * kBS <= kThresh);
+  if (single_pass) return launch_h16<T, 128, PA_V1_D128_NW, PA_V1_D128_TB>(P, trace, grid, L);
+  if ((int64_t)grid.x <= kSmallGrid) return launch_h16<T, 128, 4, 1>(P, trace, grid, L);
+  return launch_h16<T, 128, PA_BF16_D128_NW, PA_BF16_D128_TB>(P, trace, grid, L);
 }
 
-hipError_t launch_partitions(const Params& P, int D, int dtype, bool trace, hipStream_t stream) {
+hipError_t launch_partitions(const Params& P, int D, int dtype, bool trace, const Launch& stream) {
   const int64_t pgrid = (P.mode == PA_MODE_V1) ? 1 : P.Pmax;
   const dim3 grid((unsigned)((int64_t)P.S * P.Hkv * pgrid));
-  if (grid.x == 0) return hipSuccess;
+  if (grid.x == 0) return nothing_launched(stream);
   if (dtype == PA_BF16) {
     if (D == 128) return launch_h16_d128<__bf16>(P, trace, grid, stream);
     return launch_h16<__bf16, 256, PA_BF16_D256_NW, PA_BF16_D256_TB>(P, trace, grid, stream);
@@ -989,8 +1036,22 @@ hipError_t launch_partitions(const Params& P, int D, int dtype, bool trace, hipS
 // at least kReduceMinWGs workgroups, 32 floats at the narrowest.
 constexpr int64_t kReduceMinWGs = 2048;
 
+// Partial sets up to this size (tmp_out bytes) are reduced with speculative
+// first loads: the kernel is then latency-bound and the loads it may waste
+// (partitions past a short sequence's end) are few.
+#ifndef PA_REDUCE_SPEC_BYTES
+#define PA_REDUCE_SPEC_BYTES (8 << 20)
+#endif
+constexpr int64_t kReduceSpecBytes = PA_REDUCE_SPEC_BYTES;
+
+template <typename T, int CW>
+hipError_t launch_reduce_cw(bool spec, dim3 grid, dim3 block, const Launch& L, const ReduceParams& R) {
+  if (spec) return launch(pa_lse_reduce_kernel<T, CW, true>, grid, block, 0, L, R);
+  return launch(pa_lse_reduce_kernel<T, CW, false>, grid, block, 0, L, R);
+}
+
 template <typename T>
-hipError_t launch_reduce_t(const ReduceParams& R, hipStream_t stream) {
+hipError_t launch_reduce_t(const ReduceParams& R, const Launch& L) {
   const int64_t rows = (int64_t)R.S * R.H;
   int cw = 32;
   for (int c : {256, 128, 64}) {
@@ -1000,20 +1061,21 @@ hipError_t launch_reduce_t(const ReduceParams& R, hipStream_t stream) {
     }
   }
   const dim3 grid((unsigned)(rows * (R.D / cw)));
-  if (grid.x == 0) return hipSuccess;
+  if (grid.x == 0) return nothing_launched(L);
+  const dim3 block(kReduceThreads);
+  const bool spec = rows * R.Pmax * R.D * (int64_t)sizeof(float) <= kReduceSpecBytes;
   switch (cw) {
-    case 256: hipLaunchKernelGGL((pa_lse_reduce_kernel<T, 256>), grid, dim3(kReduceThreads), 0, stream, R); break;
-    case 128: hipLaunchKernelGGL((pa_lse_reduce_kernel<T, 128>), grid, dim3(kReduceThreads), 0, stream, R); break;
-    case 64: hipLaunchKernelGGL((pa_lse_reduce_kernel<T, 64>), grid, dim3(kReduceThreads), 0, stream, R); break;
-    default: hipLaunchKernelGGL((pa_lse_reduce_kernel<T, 32>), grid, dim3(kReduceThreads), 0, stream, R); break;
+    case 256: return launch_reduce_cw<T, 256>(spec, grid, block, L, R);
+    case 128: return launch_reduce_cw<T, 128>(spec, grid, block, L, R);
+    case 64: return launch_reduce_cw<T, 64>(spec, grid, block, L, R);
+    default: return launch_reduce_cw<T, 32>(spec, grid, block, L, R);
   }
-  return hipGetLastError();
 }
 
-hipError_t launch_reduce(const ReduceParams& R, int dtype, hipStream_t stream) {
-  if (dtype == PA_BF16) return launch_reduce_t<__bf16>(R, stream);
-  if (dtype == PA_F16) return launch_reduce_t<_Float16>(R, stream);
-  return launch_reduce_t<float>(R, stream);
+hipError_t launch_reduce(const ReduceParams& R, int dtype, const Launch& L) {
+  if (dtype == PA_BF16) return launch_reduce_t<__bf16>(R, L);
+  if (dtype == PA_F16) return launch_reduce_t<_Float16>(R, L);
+  return launch_reduce_t<float>(R, L);
 }
 
 Params make_params(void* out, const void* q, const void* k, const void* v, const int32_t* bt,
@@ -1039,38 +1101,47 @@ ReduceParams make_reduce_params(void* out, const float* es, const float* ml, con
   return R;
 }
 
+// No sequence can take the partitioned path: V1 forced, or AUTO with a table
+// too narrow for any context to pass the threshold (lengths are clamped to
+// the table's width).
+bool single_pass_only(const pa_shape* sh, int mode) {
+  return mode == PA_MODE_V1 || (mode == PA_MODE_AUTO && (int64_t)sh->max_blocks_per_seq * kBS <= kThresh);
+}
+
 int run_partitions(void* out, const void* q, const void* k, const void* v, const int32_t* bt,
                    const int32_t* sl, const pa_shape* sh, float scale, float* es, float* ml,
-                   float* to, int mode, int32_t* trace, int32_t* err, void* stream) {
+                   float* to, int mode, int32_t* trace, int32_t* err, const Launch& L) {
   const int st = check_all(out, q, k, v, bt, sl, sh, es, ml, to, mode, mode != PA_MODE_V1, true);
   if (st != PA_OK) return st;
   (void)hipGetLastError();
   const Params P = make_params(out, q, k, v, bt, sl, sh, scale, es, ml, to, mode, trace, err);
-  if (launch_partitions(P, sh->head_dim, sh->dtype, trace != nullptr || err != nullptr,
-                        (hipStream_t)stream) != hipSuccess)
+  if (launch_partitions(P, sh->head_dim, sh->dtype, trace != nullptr || err != nullptr, L) != hipSuccess)
     return PA_EHIP;
   return PA_OK;
 }
 
 int run_reduce(void* out, const float* es, const float* ml, const float* to, const int32_t* sl,
-               const pa_shape* sh, int mode, void* stream) {
+               const pa_shape* sh, int mode, const Launch& L) {
   const int st = check_all(out, nullptr, nullptr, nullptr, nullptr, sl, sh, es, ml, to, mode, true, false);
   if (st != PA_OK) return st;
-  if (mode == PA_MODE_V1) return PA_OK;  // nothing is partitioned
   (void)hipGetLastError();
+  if (single_pass_only(sh, mode))  // nothing is partitioned
+    return nothing_launched(L) == hipSuccess ? PA_OK : PA_EHIP;
   const ReduceParams R = make_reduce_params(out, es, ml, to, sl, sh, mode);
-  if (launch_reduce(R, sh->dtype, (hipStream_t)stream) != hipSuccess) return PA_EHIP;
+  if (launch_reduce(R, sh->dtype, L) != hipSuccess) return PA_EHIP;
   return PA_OK;
 }
+
+Launch on(void* stream) { return Launch{(hipStream_t)stream, nullptr, nullptr}; }
 
 int run_full(void* out, const void* q, const void* k, const void* v, const int32_t* bt,
              const int32_t* sl, const pa_shape* sh, float scale, float* es, float* ml, float* to,
              int mode, void* stream) {
   const int st = check_all(out, q, k, v, bt, sl, sh, es, ml, to, mode, mode != PA_MODE_V1, true);
   if (st != PA_OK) return st;
-  int rc = run_partitions(out, q, k, v, bt, sl, sh, scale, es, ml, to, mode, nullptr, nullptr, stream);
-  if (rc != PA_OK || mode == PA_MODE_V1) return rc;
-  return run_reduce(out, es, ml, to, sl, sh, mode, stream);
+  int rc = run_partitions(out, q, k, v, bt, sl, sh, scale, es, ml, to, mode, nullptr, nullptr, on(stream));
+  if (rc != PA_OK || single_pass_only(sh, mode)) return rc;
+  return run_reduce(out, es, ml, to, sl, sh, mode, on(stream));
 }
 
 }  // namespace
@@ -1103,12 +1174,29 @@ int pa_decode_partitions(void* out, const void* q, const void* k_cache, const vo
                          const pa_shape* shape, float scale, float* exp_sums, float* max_logits,
                          float* tmp_out, int mode, void* stream) {
   return run_partitions(out, q, k_cache, v_cache, block_tables, seq_lens, shape, scale, exp_sums,
-                        max_logits, tmp_out, mode, nullptr, nullptr, stream);
+                        max_logits, tmp_out, mode, nullptr, nullptr, on(stream));
 }
 
 int pa_lse_reduce(void* out, const float* exp_sums, const float* max_logits, const float* tmp_out,
                   const int32_t* seq_lens, const pa_shape* shape, int mode, void* stream) {
-  return run_reduce(out, exp_sums, max_logits, tmp_out, seq_lens, shape, mode, stream);
+  return run_reduce(out, exp_sums, max_logits, tmp_out, seq_lens, shape, mode, on(stream));
+}
+
+int pa_decode_partitions_timed(void* out, const void* q, const void* k_cache, const void* v_cache,
+                               const int32_t* block_tables, const int32_t* seq_lens,
+                               const pa_shape* shape, float scale, float* exp_sums,
+                               float* max_logits, float* tmp_out, int mode, void* start_event,
+                               void* stop_event, void* stream) {
+  return run_partitions(out, q, k_cache, v_cache, block_tables, seq_lens, shape, scale, exp_sums,
+                        max_logits, tmp_out, mode, nullptr, nullptr,
+                        Launch{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event});
+}
+
+int pa_lse_reduce_timed(void* out, const float* exp_sums, const float* max_logits, const float* tmp_out,
+                        const int32_t* seq_lens, const pa_shape* shape, int mode, void* start_event,
+                        void* stop_event, void* stream) {
+  return run_reduce(out, exp_sums, max_logits, tmp_out, seq_lens, shape, mode,
+                    Launch{(hipStream_t)stream, (hipEvent_t)start_event, (hipEvent_t)stop_event});
 }
 
 int pa_decode_partitions_debug(void* out, const void* q, const void* k_cache, const void* v_cache,
@@ -1119,7 +1207,7 @@ int pa_decode_partitions_debug(void* out, const void* q, const void* k_cache, co
   if (gather_trace && !aligned(gather_trace, 4)) return PA_EALIGN;
   if (err_flag && !aligned(err_flag, 4)) return PA_EALIGN;
   return run_partitions(out, q, k_cache, v_cache, block_tables, seq_lens, shape, scale, exp_sums,
-                        max_logits, tmp_out, mode, gather_trace, err_flag, stream);
+                        max_logits, tmp_out, mode, gather_trace, err_flag, on(stream));
 }
 
 int64_t pa_max_partitions(const pa_shape* shape) {

@@ -383,3 +383,58 @@ def test_data_errors_are_flagged_not_faulted(dev):
                                   x.scale, es, ml, to, pa.MODE_AUTO, None, err)
     torch.cuda.synchronize(dev)
     assert int(err.item()) == 3
+
+
+@pytest.mark.parametrize("mode", MODES)
+def test_timed_entry_points_match_untimed(dev, mode):
+    """The *_timed forms run the same kernels: bitwise equal outputs, and both
+    event pairs complete (also where the reduce has nothing to launch)."""
+    x = W.make_inputs(W.CONFIGS[2], seed=19, seq_lens=[5, 3000, 8192, 8193, 40000])
+    d = W.to_device(x, dev)
+    say(f"timed entry points, mode {mode}")
+    m = {"auto": pa.MODE_AUTO, "v1": pa.MODE_V1, "v2": pa.MODE_V2}[mode]
+    args = (d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens"], x.scale)
+    sh = pa.make_shape(d["q"], d["k_cache"], d["block_tables"])
+    outs = []
+    hev = pa.HipEvents()
+    try:
+        for timed in (False, True):
+            out = torch.full_like(d["q"], float("nan"))
+            es, ml, to = pa.alloc_partials(sh, dev)
+            if timed:
+                ev = [hev.new() for _ in range(4)]
+                pa.pa_decode_partitions_timed(out, *args, es, ml, to, m, ev[0], ev[1])
+                pa.pa_lse_reduce_timed(out, es, ml, to, d["seq_lens"], sh, m, ev[2], ev[3])
+            else:
+                pa.pa_decode_partitions(out, *args, es, ml, to, m)
+                pa.pa_lse_reduce(out, es, ml, to, d["seq_lens"], sh, m)
+            torch.cuda.synchronize(dev)
+            outs.append(W.from_device(out))
+        k1, k2 = hev.ms(ev[0], ev[1]), hev.ms(ev[2], ev[3])
+        say(f"  partition {k1 * 1e3:.1f} us, reduce {k2 * 1e3:.1f} us")
+        assert k1 > 0 and k2 >= 0
+        if mode == "v1":
+            assert k2 < 0.05  # nothing launched: the two marks are back to back
+    finally:
+        hev.close()
+    assert np.array_equal(outs[0], outs[1])
+    assert_close(x, torch.from_numpy(outs[1]).to(dev))
+
+
+def test_timed_entry_points_on_an_empty_batch(dev):
+    x = W.make_inputs(W.CONFIGS[2], seed=20, seq_lens=[7])
+    d = W.to_device(x, dev)
+    q0 = d["q"][:0]
+    out = torch.empty_like(q0)
+    sh = pa.make_shape(q0, d["k_cache"], d["block_tables"][:0])
+    es, ml, to = pa.alloc_partials(sh, dev)
+    hev = pa.HipEvents()
+    try:
+        ev = [hev.new() for _ in range(4)]
+        pa.pa_decode_partitions_timed(out, q0, d["k_cache"], d["v_cache"], d["block_tables"][:0],
+                                      d["seq_lens"][:0], x.scale, es, ml, to, pa.MODE_AUTO, ev[0], ev[1])
+        pa.pa_lse_reduce_timed(out, es, ml, to, d["seq_lens"][:0], sh, pa.MODE_AUTO, ev[2], ev[3])
+        torch.cuda.synchronize(dev)
+        assert hev.ms(ev[0], ev[1]) >= 0 and hev.ms(ev[2], ev[3]) >= 0
+    finally:
+        hev.close()
