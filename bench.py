@@ -17,14 +17,17 @@ Prints ONE JSON line (per workload with --all):
                against 8 TB/s. The duration comes from HIP events that the
                library records at the start and the end of that kernel's own
                dispatch (pa_decode_partitions_timed), on the launch stream,
-               over the same scrubbed steps: the profiler's per-dispatch
-               duration, without the event markers' own latency.
+               over the same scrubbed steps; it reads about 1 us above the
+               profiler's per-dispatch average (the attached events' cost),
+               far less than separate event markers (~5 us).
   cpu_baseline the fp64 oracle timed on this host's cores (bounded sample)
 
 --cold-only runs just the warmup and the timed scrubbed steps (for a
 profiler run whose per-dispatch averages then cover cold calls only);
 --copy-calibration MiB runs a plain device-to-device copy of that size, the
-reference for scaling the FETCH_SIZE / WRITE_SIZE counters.
+reference for scaling the FETCH_SIZE / WRITE_SIZE counters;
+--partition-size 256 measures the opt-in 256-token partitions (not the
+headline: 512 is the method's size).
 """
 from __future__ import annotations
 
@@ -57,7 +60,7 @@ def kernel_source_hash() -> str:
     return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
 
 
-def workload_label(x) -> dict:
+def workload_label(x, ps: int = 512) -> dict:
     c = x.cfg
     lens = x.seq_lens
     n_v2 = int((lens > 8192).sum())
@@ -67,7 +70,7 @@ def workload_label(x) -> dict:
         "head_dim": c.head_dim, "block_size": 16, "cache_dtype": c.dtype,
         "seq_lens": "x".join(map(str, lens.tolist())) if lens.size <= 4 else
                     f"{c.lengths[0]}{list(c.lengths[1:])}: sum={int(lens.sum())} min={int(lens.min())} max={int(lens.max())}",
-        "seqs_on_v2": n_v2, "partition_size": 512, "v2_threshold": 8192,
+        "seqs_on_v2": n_v2, "partition_size": ps, "v2_threshold": 8192,
         "seed": x.seed,
     }
 
@@ -151,7 +154,8 @@ def cpu_baseline(x, gpu_out, budget_s: float):
     }
 
 
-def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float, dev, cold_only=False):
+def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float, dev, cold_only=False,
+              ps: int = 512):
     import torch
 
     import paged_attention_decode_06_amd as pa
@@ -164,7 +168,7 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
     d = W.to_device(x, dev)
     q, kc, vc, bt, sl = d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens"]
     out = torch.empty_like(q)
-    sh = pa.make_shape(q, kc, bt)
+    sh = pa.make_shape(q, kc, bt, ps)
     es, ml, to = pa.alloc_partials(sh, dev)
     elem = 4 if x.cfg.dtype == "f32" else 2
     step_bytes = W.algorithmic_bytes(x.seq_lens, x.cfg.num_heads, x.cfg.num_kv_heads, x.cfg.head_dim, elem)
@@ -173,7 +177,7 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
     stream = torch.cuda.current_stream(dev)
 
     def step():
-        pa.pa_decode(out, q, kc, vc, bt, sl, x.scale, es, ml, to, stream=stream)
+        pa.pa_decode(out, q, kc, vc, bt, sl, x.scale, es, ml, to, stream=stream, partition_size=ps)
 
     sink = torch.empty((), dtype=torch.float32, device=dev)
 
@@ -199,7 +203,7 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
     wall = time.perf_counter() - wall0
     ms = np.array([a.elapsed_time(b) for a, b in ev])
     if cold_only:
-        return {"config": workload_label(x), "us_per_step": round(float(ms.mean()) * 1e3, 2)}
+        return {"config": workload_label(x, ps), "us_per_step": round(float(ms.mean()) * 1e3, 2)}
 
     # --- per-kernel durations: the same scrubbed steps, each kernel launched
     #     with events attached to its own dispatch
@@ -209,7 +213,7 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
         do_scrub(i)
         a, b, c, d_ = marks[i]
         pa.pa_decode_partitions_timed(out, q, kc, vc, bt, sl, x.scale, es, ml, to, pa.MODE_AUTO, a, b,
-                                      stream=stream)
+                                      stream=stream, partition_size=ps)
         pa.pa_lse_reduce_timed(out, es, ml, to, sl, sh, pa.MODE_AUTO, c, d_, stream=stream)
     torch.cuda.synchronize(dev)
     k1 = np.array([hev.ms(m[0], m[1]) for m in marks])
@@ -218,7 +222,8 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
     k1_ms, k2_ms = float(k1.mean()), float(k2.mean())
 
     def partitions():
-        pa.pa_decode_partitions(out, q, kc, vc, bt, sl, x.scale, es, ml, to, pa.MODE_AUTO, stream=stream)
+        pa.pa_decode_partitions(out, q, kc, vc, bt, sl, x.scale, es, ml, to, pa.MODE_AUTO, stream=stream,
+                                partition_size=ps)
 
     def reduce():
         pa.pa_lse_reduce(out, es, ml, to, sl, sh, pa.MODE_AUTO, stream=stream)
@@ -264,7 +269,7 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
         "vs_baseline": None,
         "dtype": x.cfg.dtype,
         "data": "synthetic",
-        "config": workload_label(x),
+        "config": workload_label(x, ps),
         "us_per_step": round(ms_step * 1e3, 2),
         "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
         "us_per_step_p10_p50_p90": [round(float(np.percentile(ms, p)) * 1e3, 2) for p in (10, 50, 90)],
@@ -286,7 +291,7 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
             "peak": PEAK_GBS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
-            "traffic": traffic_for(num),
+            "traffic": traffic_for(num) if ps == 512 else None,
             "kernel": "pa_partition",
             "algorithmic_bytes_per_launch": int(pk_bytes),
         },
@@ -312,6 +317,8 @@ def main(argv=None):
     ap.add_argument("--no-scrub", action="store_true", help="skip the cache scrub (warm-cache timing)")
     ap.add_argument("--cpu-budget", type=float, default=12.0, help="seconds of oracle timing (0 = skip)")
     ap.add_argument("--cold-only", action="store_true", help="only warmup + timed scrubbed steps (profiler runs)")
+    ap.add_argument("--partition-size", type=int, default=512, choices=(256, 512),
+                    help="V2 partition size (512, the default; 256 is the opt-in alternative)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args(argv)
@@ -340,7 +347,8 @@ def main(argv=None):
     pa.load()
     nums = [1, 2, 3, 4, 5] if args.all else [args.config]
     for n in nums:
-        res = bench_one(n, args.steps, args.warmup, not args.no_scrub, args.cpu_budget, dev, args.cold_only)
+        res = bench_one(n, args.steps, args.warmup, not args.no_scrub, args.cpu_budget, dev, args.cold_only,
+                        args.partition_size)
         print(json.dumps(res), flush=True)
     return 0
 

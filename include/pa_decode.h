@@ -29,7 +29,8 @@
  *     exp_sums     [S, H, Pmax]              float32  (V2 partials)
  *     max_logits   [S, H, Pmax]              float32
  *     tmp_out      [S, H, Pmax, D]           float32
- * with Pmax = ceil(max_blocks_per_seq * 16 / 512) (pa_max_partitions()).
+ * with Pmax = ceil(max_blocks_per_seq * 16 / PS) (pa_max_partitions()), PS the
+ * partition size of the shape (512 unless the shape opts into 256).
  *
  * Memory and ownership: every array pointer is a device pointer owned by the
  * caller, 16-byte aligned. The library never allocates, frees or
@@ -70,7 +71,7 @@ typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
 typedef enum {
   PA_MODE_AUTO = 0, /* per sequence: seq_len > 8192 -> V2, else V1 ([cd0d9e1a] rewrite, item 2) */
   PA_MODE_V1 = 1,   /* every sequence in one pass over its whole context */
-  PA_MODE_V2 = 2    /* every sequence in 512-token partitions + log-sum-exp reduce */
+  PA_MODE_V2 = 2    /* every sequence in partitions (512 tokens) + log-sum-exp reduce */
 } pa_mode;
 
 typedef struct {
@@ -82,18 +83,26 @@ typedef struct {
   int32_t max_blocks_per_seq; /* table width (>= 1) */
   int64_t num_blocks;         /* pool size (>= 1) */
   int32_t dtype;              /* pa_dtype */
+  int32_t partition_size;     /* tokens per V2 partition: 0 (= PA_PARTITION_SIZE, 512) or 256.
+                               * [prefix-doc] partition-size note: both sizes existed
+                               * before 512 was made the one size; 256 is opt-in here.
+                               * It changes the partials' layout (Pmax) and the
+                               * rounding order, not the definition. The V1/V2
+                               * threshold stays 8192 tokens. */
 } pa_shape;
 
 enum {
   PA_OK = 0,
   PA_EINVAL = -1,       /* null pointer, negative or inconsistent size, H % Hkv != 0 */
-  PA_EUNSUPPORTED = -2, /* D not 128/256, block_size != 16, G > 16, unknown dtype/mode */
+  PA_EUNSUPPORTED = -2, /* D not 128/256, block_size != 16, G > 16, unknown dtype/mode,
+                         partition_size not 0/256/512 */
   PA_EALIGN = -3,       /* a pointer is not 16-byte aligned */
   PA_EHIP = -4          /* the HIP launch failed */
 };
 
 #define PA_BLOCK_SIZE 16
 #define PA_PARTITION_SIZE 512 /* [cd0d9e1a] V2 implementation; [prefix-doc] partition-size note */
+#define PA_PARTITION_SIZE_SMALL 256 /* the opt-in alternative (pa_shape.partition_size) */
 #define PA_V2_THRESHOLD 8192  /* [cd0d9e1a] rewrite, item 2 */
 
 /* Single pass over every sequence's whole context ([cd0d9e1a] V1 discussion
@@ -105,7 +114,8 @@ int pa_decode_v1(void* out, const void* q, const void* k_cache, const void* v_ca
 /* Two phases for every sequence ([cd0d9e1a] V2 implementation): phase 1
  * writes per-partition max_logits (natural-log units of the scaled logits),
  * exp_sums (relative to that max) and tmp_out (normalised by its exp_sum) for
- * p < ceil(seq_len / 512); phase 2 combines them into out. */
+ * p < ceil(seq_len / PS) (PS = 512, or 256 when the shape opts in); phase 2
+ * combines them into out. */
 int pa_decode_v2(void* out, const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* block_tables, const int32_t* seq_lens, const pa_shape* shape,
                  float scale, float* exp_sums, float* max_logits, float* tmp_out, void* stream);
@@ -128,7 +138,7 @@ int pa_decode_partitions(void* out, const void* q, const void* k_cache, const vo
 /* Phase 2 alone ([cd0d9e1a] V2 implementation, phase 2): for each sequence
  * the mode sends to V2 (every sequence under PA_MODE_V2, seq_len > 8192 under
  * PA_MODE_AUTO), M = max_p max_logits, c_p = exp(max_logits_p - M) *
- * exp_sums_p, out = sum_p c_p tmp_out_p / sum_p c_p over p < ceil(seq_len/512).
+ * exp_sums_p, out = sum_p c_p tmp_out_p / sum_p c_p over p < ceil(seq_len/PS).
  * Other sequences' out rows are left untouched. */
 int pa_lse_reduce(void* out, const float* exp_sums, const float* max_logits, const float* tmp_out,
                   const int32_t* seq_lens, const pa_shape* shape, int mode, void* stream);
@@ -159,7 +169,7 @@ int pa_lse_reduce_timed(void* out, const float* exp_sums, const float* max_logit
                         const int32_t* seq_lens, const pa_shape* shape, int mode, void* start_event,
                         void* stop_event, void* stream);
 
-/* Pmax = ceil(max_blocks_per_seq * 16 / 512), or a negative status. */
+/* Pmax = ceil(max_blocks_per_seq * 16 / PS), or a negative status. */
 int64_t pa_max_partitions(const pa_shape* shape);
 
 /* Element counts of the partial buffers: which = 0 for exp_sums and

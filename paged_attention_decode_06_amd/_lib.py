@@ -30,6 +30,7 @@ class PaShape(ctypes.Structure):
         ("max_blocks_per_seq", ctypes.c_int32),
         ("num_blocks", ctypes.c_int64),
         ("dtype", ctypes.c_int32),
+        ("partition_size", ctypes.c_int32),
     ]
 
 
@@ -103,15 +104,18 @@ def _dtype_code(dt) -> int:
     raise PaError(PA_EUNSUPPORTED, f"dtype {dt}")
 
 
-def make_shape(q, k_cache, block_tables) -> PaShape:
-    """pa_shape from q [S, H, D], k_cache [NB, Hkv, 16, D], block_tables [S, MB]."""
+def make_shape(q, k_cache, block_tables, partition_size: int = 0) -> PaShape:
+    """pa_shape from q [S, H, D], k_cache [NB, Hkv, 16, D], block_tables [S, MB].
+
+    partition_size 0 means the default (512 tokens); 256 opts into the smaller
+    partitions."""
     S, H, D = q.shape
     NB, Hkv, BS, D2 = k_cache.shape
     if D2 != D:
         raise PaError(PA_EINVAL, f"head_dim of q ({D}) and cache ({D2}) differ")
     if block_tables.dim() != 2 or block_tables.shape[0] != S:
         raise PaError(PA_EINVAL, "block_tables must be [num_seqs, max_blocks_per_seq]")
-    return PaShape(S, H, Hkv, D, BS, block_tables.shape[1], NB, _dtype_code(q.dtype))
+    return PaShape(S, H, Hkv, D, BS, block_tables.shape[1], NB, _dtype_code(q.dtype), int(partition_size))
 
 
 def _ptr(t):
@@ -178,9 +182,10 @@ def pa_decode_v1(out, q, k_cache, v_cache, block_tables, seq_lens, scale, stream
                                               float(scale), _stream(stream, q.device)))
 
 
-def _full(name, out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits, tmp_out, stream):
+def _full(name, out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits, tmp_out, stream,
+          partition_size):
     _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens, (exp_sums, max_logits, tmp_out))
-    sh = make_shape(q, k_cache, block_tables)
+    sh = make_shape(q, k_cache, block_tables, partition_size)
     fn = getattr(load(), name)
     _call(name, fn(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
                    ctypes.byref(sh), float(scale), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out),
@@ -188,21 +193,21 @@ def _full(name, out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sum
 
 
 def pa_decode_v2(out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits, tmp_out,
-                 stream=None):
+                 stream=None, partition_size=0):
     _full("pa_decode_v2", out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits,
-          tmp_out, stream)
+          tmp_out, stream, partition_size)
 
 
 def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits, tmp_out,
-              stream=None):
+              stream=None, partition_size=0):
     _full("pa_decode", out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits,
-          tmp_out, stream)
+          tmp_out, stream, partition_size)
 
 
 def pa_decode_partitions(out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits,
-                         tmp_out, mode, stream=None):
+                         tmp_out, mode, stream=None, partition_size=0):
     _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens, (exp_sums, max_logits, tmp_out))
-    sh = make_shape(q, k_cache, block_tables)
+    sh = make_shape(q, k_cache, block_tables, partition_size)
     _call("pa_decode_partitions", load().pa_decode_partitions(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
         ctypes.byref(sh), float(scale), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), int(mode),
@@ -210,9 +215,9 @@ def pa_decode_partitions(out, q, k_cache, v_cache, block_tables, seq_lens, scale
 
 
 def pa_decode_partitions_debug(out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits,
-                               tmp_out, mode, gather_trace=None, err_flag=None, stream=None):
+                               tmp_out, mode, gather_trace=None, err_flag=None, stream=None, partition_size=0):
     _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens, (exp_sums, max_logits, tmp_out))
-    sh = make_shape(q, k_cache, block_tables)
+    sh = make_shape(q, k_cache, block_tables, partition_size)
     _call("pa_decode_partitions_debug", load().pa_decode_partitions_debug(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
         ctypes.byref(sh), float(scale), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), int(mode),
@@ -227,10 +232,10 @@ def pa_lse_reduce(out, exp_sums, max_logits, tmp_out, seq_lens, shape: PaShape, 
 
 
 def pa_decode_partitions_timed(out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits,
-                               tmp_out, mode, start_event, stop_event, stream=None):
+                               tmp_out, mode, start_event, stop_event, stream=None, partition_size=0):
     """Phase 1 with raw hipEvent_t handles (ints) recorded around the kernel itself."""
     _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens, (exp_sums, max_logits, tmp_out))
-    sh = make_shape(q, k_cache, block_tables)
+    sh = make_shape(q, k_cache, block_tables, partition_size)
     _call("pa_decode_partitions_timed", load().pa_decode_partitions_timed(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
         ctypes.byref(sh), float(scale), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), int(mode),

@@ -7,6 +7,9 @@
 //     partition and keeps its max logit, exp-sum and output; phase 2 combines
 //     partitions with log-sum-exp weights. Inside a partition the softmax is
 //     the running (online) form, the same blocking flash attention uses.
+//   * Partition size: 512 tokens. The prefix-prefill patch docstring (project_6
+//     blame of optimizations/prefix_prefill_patch.py) records 256 as the other
+//     size once in use; a shape may opt into it (pa_shape.partition_size).
 //
 // Kernel design (gfx950, wave64):
 //   One workgroup per (sequence, KV head, partition); partition is the slowest
@@ -22,7 +25,7 @@
 //       accumulator itself (rounded to bf16), and V is loaded as whole rows
 //       (16 lanes x 16 B = one 256-byte row) and transposed in registers.
 //   Waves then merge (max, exp-sum, output) through LDS in a fixed order and
-//   wave 0 writes either out (V1) or the three partials (V2).
+//   the workgroup writes either out (V1) or the three partials (V2).
 //
 // Data errors never turn into out-of-bounds accesses: contexts are cut to the
 // table width and out-of-range block ids are read as block 0 (both reported
@@ -69,6 +72,7 @@ struct Params {
   int32_t* err;
   int64_t NB;
   int S, H, Hkv, G, MB, Pmax, mode;
+  int PS;        // tokens per partition (512, or the opt-in 256)
   float scale2;  // softmax scale times log2(e): logits are kept in base-2 units
 };
 
@@ -113,10 +117,10 @@ __device__ __forceinline__ int work_range(const Params& P, int s, int p, Range& 
   if (L < 0) L = 0;
   r.v2 = (P.mode == PA_MODE_V2) || (P.mode == PA_MODE_AUTO && L > kThresh);
   if (r.v2) {
-    const int np = (L + kPart - 1) / kPart;
+    const int np = (L + P.PS - 1) / P.PS;
     if (p >= np) return 0;
-    r.tok_begin = p * kPart;
-    r.tok_end = min(r.tok_begin + kPart, L);
+    r.tok_begin = p * P.PS;
+    r.tok_end = min(r.tok_begin + P.PS, L);
   } else {
     if (p != 0) return 0;
     if (L == 0) return 2;
@@ -411,7 +415,7 @@ void pa_partition_h16(Params P) {
   const int32_t* bt_row = P.bt + (int64_t)s * P.MB;
   // The first block-id list, read speculatively (a single pass starts at block
   // 0, partition p at block 32p; a workgroup with nothing to do drops it).
-  int ids = read_block_ids<TB>(P, bt_row, (P.mode == PA_MODE_V1) ? 0 : p * (kPart / kBS), t0, dt, 0, lane);
+  int ids = read_block_ids<TB>(P, bt_row, (P.mode == PA_MODE_V1) ? 0 : p * (P.PS / kBS), t0, dt, 0, lane);
   Range r;
   const int what = work_range(P, s, p, r);
   if (what == 0) return;
@@ -774,7 +778,7 @@ struct ReduceParams {
   const float* max_logits;
   const float* tmp_out;
   const int32_t* sl;
-  int S, H, MB, Pmax, mode, D;
+  int S, H, MB, Pmax, mode, D, PS;
 };
 
 template <typename T, int CW, bool SPEC>
@@ -815,7 +819,7 @@ __global__ __launch_bounds__(kReduceThreads) void pa_lse_reduce_kernel(ReducePar
   if (L > R.MB * kBS) L = R.MB * kBS;
   if (L < 0) L = 0;
   if (R.mode == PA_MODE_AUTO && L <= kThresh) return;
-  const int np = (L + kPart - 1) / kPart;
+  const int np = (L + R.PS - 1) / R.PS;
 
   float M = -INFINITY, ctot = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -913,11 +917,17 @@ int check_shape(const pa_shape* sh) {
   if (sh->block_size != kBS) return PA_EUNSUPPORTED;
   if (sh->dtype != PA_F32 && sh->dtype != PA_BF16 && sh->dtype != PA_F16) return PA_EUNSUPPORTED;
   if (sh->max_blocks_per_seq > (1 << 26)) return PA_EUNSUPPORTED;  // keeps token counts in int32
+  if (sh->partition_size != 0 && sh->partition_size != PA_PARTITION_SIZE &&
+      sh->partition_size != PA_PARTITION_SIZE_SMALL)
+    return PA_EUNSUPPORTED;
   return PA_OK;
 }
 
+int partition_size(const pa_shape* sh) { return sh->partition_size ? sh->partition_size : kPart; }
+
 int64_t max_partitions(const pa_shape* sh) {
-  return ((int64_t)sh->max_blocks_per_seq * kBS + kPart - 1) / kPart;
+  const int64_t ps = partition_size(sh);
+  return ((int64_t)sh->max_blocks_per_seq * kBS + ps - 1) / ps;
 }
 
 int check_all(const void* out, const void* q, const void* k, const void* v, const int32_t* bt,
@@ -1087,7 +1097,7 @@ Params make_params(void* out, const void* q, const void* k, const void* v, const
   P.NB = sh->num_blocks;
   P.S = sh->num_seqs; P.H = sh->num_heads; P.Hkv = sh->num_kv_heads;
   P.G = sh->num_heads / sh->num_kv_heads; P.MB = sh->max_blocks_per_seq;
-  P.Pmax = (int)max_partitions(sh); P.mode = mode;
+  P.Pmax = (int)max_partitions(sh); P.mode = mode; P.PS = partition_size(sh);
   P.scale2 = scale * kLog2e;
   return P;
 }
@@ -1097,7 +1107,7 @@ ReduceParams make_reduce_params(void* out, const float* es, const float* ml, con
   ReduceParams R;
   R.out = out; R.exp_sums = es; R.max_logits = ml; R.tmp_out = to; R.sl = sl;
   R.S = sh->num_seqs; R.H = sh->num_heads; R.MB = sh->max_blocks_per_seq;
-  R.Pmax = (int)max_partitions(sh); R.mode = mode; R.D = sh->head_dim;
+  R.Pmax = (int)max_partitions(sh); R.mode = mode; R.D = sh->head_dim; R.PS = partition_size(sh);
   return R;
 }
 

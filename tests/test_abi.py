@@ -66,6 +66,9 @@ def test_valid_args_pass(lib):
     (dict(block_size=32), L.PA_EUNSUPPORTED),
     (dict(dtype=7), L.PA_EUNSUPPORTED),
     (dict(num_heads=34, num_kv_heads=2), L.PA_EUNSUPPORTED),   # G = 17 > 16
+    (dict(partition_size=300), L.PA_EUNSUPPORTED),             # only 512 (0) and 256
+    (dict(partition_size=128), L.PA_EUNSUPPORTED),
+    (dict(partition_size=-512), L.PA_EUNSUPPORTED),
 ])
 def test_bad_shapes(lib, kw, status):
     assert check(lib, shape(**kw)) == status
@@ -123,6 +126,27 @@ def test_partition_arithmetic(lib):
     assert lib.pa_partials_elems(ctypes.byref(sh), 1) == 3 * 16 * 64 * 256
     assert lib.pa_partials_elems(ctypes.byref(sh), 5) == L.PA_EINVAL
     assert lib.pa_max_partitions(ctypes.byref(shape(head_dim=5))) == L.PA_EUNSUPPORTED
+
+
+def test_opt_in_partition_size(lib):
+    """partition_size 0 is the 512-token default; 256 doubles the partition count."""
+    assert check(lib, shape(partition_size=256)) == L.PA_OK
+    assert check(lib, shape(partition_size=512)) == L.PA_OK
+    for mb, p512, p256 in [(6250, 196, 391), (16, 1, 1), (32, 1, 2), (33, 2, 3), (2048, 64, 128)]:
+        assert lib.pa_max_partitions(ctypes.byref(shape(max_blocks_per_seq=mb))) == p512
+        assert lib.pa_max_partitions(ctypes.byref(shape(max_blocks_per_seq=mb, partition_size=512))) == p512
+        assert lib.pa_max_partitions(ctypes.byref(shape(max_blocks_per_seq=mb, partition_size=256))) == p256
+    sh = shape(num_seqs=3, max_blocks_per_seq=2048, head_dim=256, partition_size=256)
+    assert lib.pa_partials_elems(ctypes.byref(sh), 1) == 3 * 16 * 128 * 256
+
+
+def test_shape_struct_layout():
+    """The binding's struct matches the header's field order (40 bytes, the
+    partition size filling what was tail padding)."""
+    assert ctypes.sizeof(L.PaShape) == 40
+    assert L.PaShape.num_blocks.offset == 24
+    assert L.PaShape.dtype.offset == 32
+    assert L.PaShape.partition_size.offset == 36
 
 
 def test_status_strings(lib):

@@ -33,21 +33,22 @@ def say(*a):
     print(*a, flush=True)
 
 
-def run(x, dev, mode="auto", d=None):
-    """Run one decode; returns (out, (exp_sums, max_logits, tmp_out)) as device tensors."""
+def run(x, dev, mode="auto", d=None, ps=0):
+    """Run one decode (ps: partition size, 0 = the 512 default); returns
+    (out, (exp_sums, max_logits, tmp_out)) as device tensors."""
     d = d or W.to_device(x, dev)
     out = torch.full_like(d["q"], float("nan"))
-    sh = pa.make_shape(d["q"], d["k_cache"], d["block_tables"])
+    sh = pa.make_shape(d["q"], d["k_cache"], d["block_tables"], ps)
     es, ml, to = pa.alloc_partials(sh, dev)
     for t in (es, ml, to):
         t.fill_(float("nan"))
     args = (out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens"], x.scale)
     if mode == "auto":
-        pa.pa_decode(*args, es, ml, to)
+        pa.pa_decode(*args, es, ml, to, partition_size=ps)
     elif mode == "v1":
         pa.pa_decode_v1(*args)
     elif mode == "v2":
-        pa.pa_decode_v2(*args, es, ml, to)
+        pa.pa_decode_v2(*args, es, ml, to, partition_size=ps)
     else:
         raise ValueError(mode)
     torch.cuda.synchronize(dev)
@@ -290,25 +291,27 @@ def test_gather_trace_matches_oracle_exactly(dev, mode, width):
     assert int(err.item()) == 0
 
 
+@pytest.mark.parametrize("ps", [512, 256])
 @pytest.mark.parametrize("width", WIDTHS)
-def test_partials_match_oracle_partition_stats(dev, width):
-    lens = [1100, 513, 9000, 1]
+def test_partials_match_oracle_partition_stats(dev, width, ps):
+    lens = [1100, 513, 9000, 1, 257]
     x = W.make_inputs(W.CONFIGS[2], seed=23, seq_lens=lens, max_blocks_per_seq=width)
     d = W.to_device(x, dev)
-    sh = pa.make_shape(d["q"], d["k_cache"], d["block_tables"])
+    sh = pa.make_shape(d["q"], d["k_cache"], d["block_tables"], ps)
     es, ml, to = pa.alloc_partials(sh, dev)
     for t in (es, ml, to):
         t.fill_(float("nan"))
     out = torch.empty_like(d["q"])
-    say("V2 partials vs oracle")
+    say(f"V2 partials vs oracle, partition size {ps}")
     pa.pa_decode_partitions(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens"], x.scale,
-                            es, ml, to, pa.MODE_V2)
+                            es, ml, to, pa.MODE_V2, partition_size=ps)
     torch.cuda.synchronize(dev)
+    assert es.shape[2] == -(-x.max_blocks_per_seq * 16 // ps)
     es, ml, to = es.cpu().numpy(), ml.cpu().numpy(), to.cpu().numpy()
     lists = oracle.gather_list(x.block_tables, x.seq_lens)
     for s, L in enumerate(lens):
-        m, l, o = oracle.partition_stats(x.q[s], x.k_cache, x.v_cache, lists[s], L, x.scale, "bf16")
-        P = oracle.num_partitions(L)
+        m, l, o = oracle.partition_stats(x.q[s], x.k_cache, x.v_cache, lists[s], L, x.scale, "bf16", ps)
+        P = oracle.num_partitions(L, ps)
         assert np.abs(ml[s, :, :P] - m).max() <= 1e-3
         assert (np.abs(es[s, :, :P] - l) / l).max() <= 1e-2
         assert max_err(to[s, :, :P], o) <= 2e-2
@@ -320,26 +323,27 @@ def test_partials_match_oracle_partition_stats(dev, width):
 REDUCE_SHAPES = [(3, 4, 128), (64, 16, 128), (128, 16, 128), (128, 16, 256)]
 
 
-@pytest.mark.parametrize("S,H,D", REDUCE_SHAPES)
+@pytest.mark.parametrize("S,H,D,ps", [(*sh, 512) for sh in REDUCE_SHAPES] + [(64, 16, 128, 256), (3, 4, 256, 256)])
 @pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
-def test_reduce_fed_with_oracle_partials(dev, dtype, S, H, D):
+def test_reduce_fed_with_oracle_partials(dev, dtype, S, H, D, ps):
     rng = np.random.default_rng(24)
-    MB = 100                               # Pmax = ceil(100*16/512) = 4
+    MB = 100                               # Pmax = ceil(100*16/ps): 4 at 512, 7 at 256
     lens = rng.integers(1, 1601, size=S).astype(np.int32)
     lens[0] = 1600
-    P = 4
+    P = -(-MB * 16 // ps)
     m = rng.normal(0, 5, (S, H, P)); l = rng.uniform(1, 50, (S, H, P)); o = rng.normal(0, 1, (S, H, P, D))
     want = np.zeros((S, H, D))
     for s in range(S):
-        n = oracle.num_partitions(int(lens[s]))
+        n = oracle.num_partitions(int(lens[s]), ps)
         for h in range(H):
             want[s, h] = oracle.lse_combine(m[s, h, :n], l[s, h, :n], o[s, h, :n])
     tdt = {"bf16": torch.bfloat16, "f16": torch.float16, "f32": torch.float32}[dtype]
     code = {"bf16": pa.PA_BF16, "f16": pa.PA_F16, "f32": pa.PA_F32}[dtype]
     out = torch.full((S, H, D), float("nan"), dtype=tdt, device=dev)
     to_t = lambda a: torch.from_numpy(a.astype(np.float32)).to(dev)
-    sh = pa.PaShape(S, H, 1, D, 16, MB, 10, code)
-    say(f"reduce from oracle partials {dtype} S={S} H={H} D={D}")
+    sh = pa.PaShape(S, H, 1, D, 16, MB, 10, code, 0 if ps == 512 else ps)
+    assert pa.max_partitions(sh) == P
+    say(f"reduce from oracle partials {dtype} S={S} H={H} D={D} partition size {ps}")
     pa.pa_lse_reduce(out, to_t(l), to_t(m), to_t(o), torch.from_numpy(lens).to(dev), sh, pa.MODE_V2)
     torch.cuda.synchronize(dev)
     assert max_err(W.from_device(out), want) <= {"bf16": 2e-2, "f16": 5e-3, "f32": 1e-5}[dtype]
@@ -438,3 +442,58 @@ def test_timed_entry_points_on_an_empty_batch(dev):
         assert hev.ms(ev[0], ev[1]) >= 0 and hev.ms(ev[2], ev[3]) >= 0
     finally:
         hev.close()
+
+
+# ---------------------------------------------------------------- opt-in 256-token partitions
+@pytest.mark.parametrize("num", [3, 5])
+def test_config_parity_partition_256(dev, num):
+    x = W.make_inputs(num)
+    say(f"config {num} {x.cfg.name} with 256-token partitions")
+    out, _ = run(x, dev, "auto", ps=256)
+    seqs = None if num <= 4 else sample_seqs(x.seq_lens, 12, np.random.default_rng(6))
+    assert np.isfinite(assert_close(x, out, seqs, "auto/256")).all()
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+@pytest.mark.parametrize("width", WIDTHS)
+@pytest.mark.parametrize("D", [128, 256])
+@pytest.mark.parametrize("mode", ["auto", "v2"])
+def test_modes_vs_oracle_partition_256(dev, D, mode, width, dtype):
+    lens = [1, 37, 255, 256, 257, 512, 513, 8192, 8193, 20000]
+    cfg = W.DecodeConfig(f"ps256-{dtype}-d{D}", len(lens), 16, 2, D, dtype, ("custom",))
+    x = W.make_inputs(cfg, seed=31, seq_lens=lens, max_blocks_per_seq=width)
+    say(f"partition 256, mode {mode} D={D} {dtype} table width={x.max_blocks_per_seq}")
+    out, _ = run(x, dev, mode, ps=256)
+    assert_close(x, out, label=f"{mode}/256")
+
+
+@pytest.mark.parametrize("mode", ["auto", "v2"])
+def test_gather_trace_partition_256(dev, mode):
+    lens = [300, 4000, 9000]
+    x = W.make_inputs(W.CONFIGS[2], seed=32, seq_lens=lens, max_blocks_per_seq=1300)
+    d = W.to_device(x, dev)
+    sh = pa.make_shape(d["q"], d["k_cache"], d["block_tables"], 256)
+    es, ml, to = pa.alloc_partials(sh, dev)
+    out = torch.empty_like(d["q"])
+    trace = torch.full(tuple(x.block_tables.shape), -7, dtype=torch.int32, device=dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    m = {"auto": pa.MODE_AUTO, "v2": pa.MODE_V2}[mode]
+    say(f"gather trace, partition 256, mode {mode}")
+    pa.pa_decode_partitions_debug(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens"],
+                                  x.scale, es, ml, to, m, trace, err, partition_size=256)
+    torch.cuda.synchronize(dev)
+    got = trace.cpu().numpy()
+    for s, ids in enumerate(oracle.gather_list(x.block_tables, x.seq_lens)):
+        assert np.array_equal(got[s, :len(ids)], ids)
+        assert (got[s, len(ids):] == -7).all()
+    assert int(err.item()) == 0
+
+
+def test_partition_256_and_512_agree(dev):
+    x = W.make_inputs(W.CONFIGS[2], seed=33, seq_lens=[9000, 30000, 100])
+    d = W.to_device(x, dev)
+    say("256 vs 512 partitions")
+    a = W.from_device(run(x, dev, "v2", d)[0])
+    b = W.from_device(run(x, dev, "v2", d, ps=256)[0])
+    assert max_err(a, b) <= 2 * TOL["bf16"]
+    assert_close(x, torch.from_numpy(b).to(dev), label="v2/256")
