@@ -258,6 +258,150 @@ def _poison(lens, tables, k, v, poison_block, dtype) -> None:
     v[unused] = nan
 
 
+# ---------------------------------------------------------------- prefix / chunked prefill
+@dataclass(frozen=True)
+class PrefillConfig:
+    """One prefix/chunked-prefill workload over the paged cache.
+
+    Sequence s holds C_s cached prefix tokens followed by Q_s chunk tokens
+    (seq_len L_s = C_s + Q_s, all of it in the cache); the chunk's Q_s query
+    tokens are packed by token into q [sum Q_s, H, D]. `context` and `chunk`
+    name the distributions of C_s and Q_s like DecodeConfig.lengths."""
+    name: str
+    num_seqs: int
+    num_heads: int
+    num_kv_heads: int
+    head_dim: int
+    dtype: str
+    context: tuple
+    chunk: tuple
+    scale: float | None = None
+
+    @property
+    def softmax_scale(self) -> float:
+        return self.scale if self.scale is not None else 1.0 / math.sqrt(self.head_dim)
+
+
+# Prefill workloads (seed = 2000 + number): the last 2048-token chunk of a
+# 100K-token prompt with its prefix cached; a batch of fresh 1024-token
+# prompts (16K batched tokens); a mixed batch of cached prefixes and chunks;
+# the same mix at head_dim 256. Chunked prefill with 8K-32K batched tokens and
+# 100K contexts is the serving setting the pages describe (prefix_prefill_patch.py
+# docstring, yaml analysis; commit 490ff98a, computility-run.yaml change).
+PREFILL_CONFIGS = {
+    1: PrefillConfig("chunk2048-ctx100K-bf16", 1, 16, 2, 128, "bf16", ("fixed", 100000 - 2048), ("fixed", 2048)),
+    2: PrefillConfig("batch16-prompt1024-bf16", 16, 16, 2, 128, "bf16", ("fixed", 0), ("fixed", 1024)),
+    3: PrefillConfig("batch8-ctxU0-32768-chunkU1-2048-bf16", 8, 16, 2, 128, "bf16",
+                     ("uniform", 0, 32768), ("uniform", 1, 2048)),
+    4: PrefillConfig("batch4-ctxU0-8192-chunk512-d256-bf16", 4, 16, 2, 256, "bf16",
+                     ("uniform", 0, 8192), ("fixed", 512)),
+}
+
+
+@dataclass
+class PrefillInputs:
+    cfg: PrefillConfig
+    seed: int
+    seq_lens: np.ndarray         # int32 [S]: C_s + Q_s tokens in the cache
+    query_lens: np.ndarray       # int32 [S]: Q_s
+    query_start_loc: np.ndarray  # int32 [S + 1]: exclusive prefix sum of query_lens
+    block_tables: np.ndarray     # int32 [S, max_blocks_per_seq]
+    q: np.ndarray                # [sum Q_s, H, D]
+    k_cache: np.ndarray
+    v_cache: np.ndarray
+    scale: float
+    extra: dict = field(default_factory=dict)
+
+    @property
+    def num_blocks(self) -> int:
+        return int(self.k_cache.shape[0])
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_tables.shape[1])
+
+    @property
+    def num_query_tokens(self) -> int:
+        return int(self.query_start_loc[-1])
+
+    @property
+    def max_query_len(self) -> int:
+        return int(self.query_lens.max(initial=0))
+
+
+def _draw(dist: tuple, n: int, rng: np.random.Generator) -> np.ndarray:
+    kind = dist[0]
+    if kind == "fixed":
+        return np.full(n, dist[1], dtype=np.int64)
+    if kind == "uniform":
+        return rng.integers(dist[1], dist[2] + 1, size=n)
+    raise ValueError(f"unknown length distribution {kind!r}")
+
+
+def make_prefill_inputs(cfg: PrefillConfig | int, seed: int | None = None, *, context_lens=None,
+                        query_lens=None, max_blocks_per_seq: int | None = None,
+                        poison: bool = False) -> PrefillInputs:
+    """Draw one prefill workload (same pool, table and value recipe as decode;
+    the prefix lengths are drawn first, then the chunk lengths)."""
+    number = None
+    if isinstance(cfg, int):
+        number = cfg
+        cfg = PREFILL_CONFIGS[cfg]
+    if seed is None:
+        seed = 2000 + (number if number is not None else 0)
+    trng = _rng(seed, _PURPOSE_TABLE)
+    if context_lens is None or query_lens is None:
+        ctx = _draw(cfg.context, cfg.num_seqs, trng)
+        ql = _draw(cfg.chunk, cfg.num_seqs, trng)
+    if context_lens is not None:
+        ctx = np.asarray(context_lens, dtype=np.int64).reshape(-1)
+    if query_lens is not None:
+        ql = np.asarray(query_lens, dtype=np.int64).reshape(-1)
+    if ctx.size != ql.size:
+        raise ValueError("context_lens and query_lens differ in length")
+    if ctx.size != cfg.num_seqs:
+        cfg = PrefillConfig(cfg.name + "-custom", int(ctx.size), cfg.num_heads, cfg.num_kv_heads,
+                            cfg.head_dim, cfg.dtype, ("custom",), ("custom",), cfg.scale)
+    lens = (ctx + ql).astype(np.int32)
+    ql = ql.astype(np.int32)
+    tables, nb = build_tables(lens, trng, None, max_blocks_per_seq)
+    S, H, Hkv, D = cfg.num_seqs, cfg.num_heads, cfg.num_kv_heads, cfg.head_dim
+    store = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[cfg.dtype]
+    nb_alloc = nb + (1 if poison else 0)
+    qsl = np.zeros(S + 1, dtype=np.int32)
+    qsl[1:] = np.cumsum(ql)
+    q = np.empty((int(qsl[-1]), H, D), dtype=store)
+    _fill_normal(q.reshape(-1), seed, _PURPOSE_Q, cfg.dtype)
+    k = np.empty((nb_alloc, Hkv, BLOCK_SIZE, D), dtype=store)
+    v = np.empty((nb_alloc, Hkv, BLOCK_SIZE, D), dtype=store)
+    _fill_normal(k[:nb].reshape(-1), seed, _PURPOSE_K, cfg.dtype)
+    _fill_normal(v[:nb].reshape(-1), seed, _PURPOSE_V, cfg.dtype)
+    extra = {}
+    if poison:
+        _poison(lens, tables, k, v, nb, cfg.dtype)
+        extra["poison_block"] = nb
+    return PrefillInputs(cfg, seed, lens, ql, qsl, tables, q, k, v, cfg.softmax_scale, extra)
+
+
+def prefill_flops(seq_lens, query_lens, num_heads: int, head_dim: int) -> int:
+    """Multiply-adds x 2 the chunk tokens' attention must do: every query row
+    (token, head) against every key it may see (pos + 1 of them), for Q.K^T and
+    for P.V: 4 * D flops per (row, key)."""
+    tot = 0
+    for L, Q in zip(np.asarray(seq_lens, dtype=np.int64), np.asarray(query_lens, dtype=np.int64)):
+        Q = int(min(Q, L))
+        first = int(L) - Q + 1                      # keys seen by the chunk's first token
+        tot += (first + int(L)) * Q // 2 if Q else 0  # sum of first .. L
+    return 4 * head_dim * num_heads * tot
+
+
+def prefill_to_device(x: PrefillInputs, device="cuda"):
+    d = to_device(x, device)
+    import torch
+    d["query_start_loc"] = torch.from_numpy(x.query_start_loc).to(device)
+    return d
+
+
 def algorithmic_bytes(seq_lens, num_heads: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
     """Bytes the decode step must move at minimum.
 

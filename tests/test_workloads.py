@@ -101,3 +101,34 @@ def test_algorithmic_bytes_matches_pages_kv_arithmetic():
 def test_algorithmic_bytes_long_context():
     # 100000 tokens x 2 KV heads x 512 B + q/out 2*16*128*2 + 6250 table entries + 1 seq_len
     assert W.algorithmic_bytes([100000], 16, 2, 128, 2) == 102_400_000 + 8192 + 25000 + 4
+
+
+# ---------------------------------------------------------------- prefill inputs
+def test_prefill_inputs_are_consistent_and_seeded():
+    for k in W.PREFILL_CONFIGS:
+        cfg = W.PREFILL_CONFIGS[k]
+        if k == 1:
+            continue   # the 100K one is exercised by the GPU tests; shape arithmetic below covers it
+        x = W.make_prefill_inputs(k)
+        S = cfg.num_seqs
+        assert x.seq_lens.shape == (S,) and x.query_lens.shape == (S,)
+        assert (x.query_lens >= 1).all() and (x.seq_lens >= x.query_lens).all()
+        assert x.query_start_loc[0] == 0 and (np.diff(x.query_start_loc) == x.query_lens).all()
+        assert x.q.shape == (int(x.query_lens.sum()), cfg.num_heads, cfg.head_dim)
+        need = (x.seq_lens + 15) // 16
+        assert x.num_blocks == int(need.sum())
+        used = np.concatenate([x.block_tables[s, :need[s]] for s in range(S)])
+        assert np.array_equal(np.sort(used), np.arange(x.num_blocks))       # a permutation of the pool
+        y = W.make_prefill_inputs(k)
+        assert np.array_equal(x.q, y.q) and np.array_equal(x.k_cache, y.k_cache)
+
+
+def test_prefill_overrides_and_flops():
+    x = W.make_prefill_inputs(W.PREFILL_CONFIGS[2], seed=5, context_lens=[0, 10, 100], query_lens=[7, 1, 33])
+    assert list(x.seq_lens) == [7, 11, 133] and list(x.query_start_loc) == [0, 7, 8, 41]
+    assert x.max_query_len == 33 and x.num_query_tokens == 41
+    # keys seen: 1..7, 11, 101..133
+    keys = sum(range(1, 8)) + 11 + sum(range(101, 134))
+    assert W.prefill_flops(x.seq_lens, x.query_lens, 16, 128) == 4 * 128 * 16 * keys
+    p = W.make_prefill_inputs(W.PREFILL_CONFIGS[2], seed=5, context_lens=[3], query_lens=[20], poison=True)
+    assert p.k_cache.shape[0] == p.num_blocks and p.extra["poison_block"] == p.num_blocks - 1
