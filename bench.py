@@ -306,6 +306,100 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
     return res
 
 
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16/fp16 MFMA
+
+
+def prefill_cpu_baseline(x, out, budget_s: float) -> dict:
+    """The fp64 oracle on sampled chunk tokens of the same workload (TFLOP/s of the same flop count)."""
+    import oracle
+    from paged_attention_decode_06_amd import workloads as W
+    got = W.from_device(out)
+    lists = oracle.gather_list(x.block_tables, x.seq_lens)
+    rng = np.random.default_rng(0)
+    order = rng.permutation(x.num_query_tokens)
+    qsl = x.query_start_loc
+    flops = 0
+    worst = 0.0
+    done = 0
+    t0 = time.perf_counter()
+    for r in order:
+        s = int(np.searchsorted(qsl, r, side="right") - 1)
+        pos = int(x.seq_lens[s]) - int(x.query_lens[s]) + int(r - qsl[s])
+        ref = oracle.attend_prefill_row(x.q[r], x.k_cache, x.v_cache, lists[s], pos, x.scale, x.cfg.dtype)
+        worst = max(worst, float(np.abs(got[r] - ref).max()))
+        flops += 4 * x.cfg.head_dim * x.cfg.num_heads * max(pos + 1, 0)
+        done += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return {"value": round(flops / el / 1e12, 6), "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 NumPy oracle, one chunk token at a time (all heads), {done} of "
+                      f"{x.num_query_tokens} tokens in {el:.1f} s", "seconds": round(el, 3),
+            "max_abs_err_vs_gpu": worst}
+
+
+def bench_prefill(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float, dev) -> dict:
+    """Prefix/chunked prefill over the paged cache: one pa_prefill launch per step."""
+    import torch
+
+    import paged_attention_decode_06_amd as pa
+    from paged_attention_decode_06_amd import workloads as W
+
+    x = W.make_prefill_inputs(num)
+    d = W.prefill_to_device(x, dev)
+    out = torch.empty_like(d["q"])
+    flops = W.prefill_flops(x.seq_lens, x.query_lens, x.cfg.num_heads, x.cfg.head_dim)
+    scrub_buf = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def step():
+        pa.pa_prefill(out, d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens"],
+                      d["query_start_loc"], x.scale, x.max_query_len, stream=stream)
+
+    for _ in range(warmup):
+        if scrub:
+            torch.sum(scrub_buf, dim=None, out=sink)
+        step()
+    torch.cuda.synchronize(dev)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        if scrub:
+            torch.sum(scrub_buf, dim=None, out=sink)
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    t = float(ms.mean())
+    tf = flops / (t * 1e-3) / 1e12
+    c = x.cfg
+    res = {
+        "metric": "prefix-prefill attention TFLOP/s over the paged cache",
+        "value": round(tf, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(t, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": c.dtype, "data": "synthetic",
+        "config": {"workload": c.name, "num_seqs": c.num_seqs, "num_heads": c.num_heads,
+                   "num_kv_heads": c.num_kv_heads, "head_dim": c.head_dim, "block_size": 16,
+                   "query_tokens": x.num_query_tokens, "max_query_len": x.max_query_len,
+                   "seq_lens": x.seq_lens.tolist()[:16], "seed": x.seed},
+        "us_per_step_p10_p50_p90": [round(float(np.percentile(ms, q_)) * 1e3, 2) for q_ in (10, 50, 90)],
+        "flops_per_step": int(flops),
+        "tokens_per_s": round(x.num_query_tokens / (t * 1e-3), 1),
+        "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "pa_prefill",
+                     "flops_per_launch": int(flops)},
+        "kernel_source_sha256_16": kernel_source_hash(),
+    }
+    res["cpu_baseline"] = prefill_cpu_baseline(x, out, cpu_budget) if cpu_budget > 0 else None
+    del scrub_buf
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,6 +413,9 @@ def main(argv=None):
     ap.add_argument("--cold-only", action="store_true", help="only warmup + timed scrubbed steps (profiler runs)")
     ap.add_argument("--partition-size", type=int, default=512, choices=(256, 512),
                     help="V2 partition size (512, the default; 256 is the opt-in alternative)")
+    ap.add_argument("--prefill", type=int, default=0, metavar="N",
+                    help="measure prefix/chunked-prefill workload N (1..4; 0 = decode); --all-prefill for all")
+    ap.add_argument("--all-prefill", action="store_true", help="every prefill workload, one JSON line each")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args(argv)
@@ -345,6 +442,11 @@ def main(argv=None):
         return 0
     import paged_attention_decode_06_amd as pa
     pa.load()
+    if args.prefill or args.all_prefill:
+        for n in ([1, 2, 3, 4] if args.all_prefill else [args.prefill]):
+            res = bench_prefill(n, args.steps, args.warmup, not args.no_scrub, args.cpu_budget, dev)
+            print(json.dumps(res), flush=True)
+        return 0
     nums = [1, 2, 3, 4, 5] if args.all else [args.config]
     for n in nums:
         res = bench_one(n, args.steps, args.warmup, not args.no_scrub, args.cpu_budget, dev, args.cold_only,

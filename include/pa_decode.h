@@ -169,6 +169,38 @@ int pa_lse_reduce_timed(void* out, const float* exp_sums, const float* max_logit
                         const int32_t* seq_lens, const pa_shape* shape, int mode, void* start_event,
                         void* stop_event, void* stream);
 
+/* Prefix / chunked-prefill attention over the same paged cache ([cd0d9e1a]
+ * "paged_attn.py rewrite" item 1: the prefix path gathers the context's K/V
+ * from the cache and walks query tiles over it with the online softmax;
+ * [prefix-doc]: query tiles against key/value tiles, head_dim 128/256, GQA,
+ * fp16/bf16, chunked prefill).
+ *
+ * Sequence s holds seq_lens[s] = L tokens in the cache; the last
+ * Q = query_start_loc[s+1] - query_start_loc[s] of them are the chunk being
+ * prefilled, their K/V already written to the cache. Chunk token i
+ * (0 <= i < Q) sits at position L - Q + i and attends to cache tokens
+ * 0 .. L - Q + i (its prefix, then the chunk causally); a token whose
+ * position is negative (Q > L) gets a zero output.
+ *
+ *   q, out           [num_query_tokens, H, D]  dtype (bf16 or fp16 only),
+ *                    packed by token: rows query_start_loc[s] .. [s+1]-1
+ *                    belong to sequence s
+ *   query_start_loc  int32 [S + 1], non-decreasing, [0] = 0,
+ *                    [S] = num_query_tokens
+ *   max_query_len    >= every Q (sizes the grid; host value, no device read)
+ *   k_cache, v_cache, block_tables, seq_lens as for decode; shape.dtype must
+ *   be PA_BF16 or PA_F16 (PA_EUNSUPPORTED otherwise); partition_size unused.
+ *
+ * Returns PA_OK with nothing launched when num_seqs, num_query_tokens or
+ * max_query_len is 0. Data errors are undefined results, never out-of-bounds
+ * accesses: query_start_loc entries are clamped to [0, num_query_tokens],
+ * seq_lens to [0, max_blocks_per_seq * 16], out-of-range block ids read block
+ * 0; chunk tokens beyond max_query_len are not computed. Bitwise
+ * reproducible for the same shape. */
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+               const int32_t* seq_lens, const int32_t* query_start_loc, const pa_shape* shape,
+               int32_t num_query_tokens, int32_t max_query_len, float scale, void* stream);
+
 /* Pmax = ceil(max_blocks_per_seq * 16 / PS), or a negative status. */
 int64_t pa_max_partitions(const pa_shape* shape);
 

@@ -8,5 +8,5 @@ from ._lib import (  # noqa: F401
     BLOCK_SIZE, HipEvents, PARTITION_SIZE, V2_THRESHOLD, MODE_AUTO, MODE_V1, MODE_V2, PA_F32, PA_BF16, PA_F16,
     PaError, PaShape, alloc_partials, load, make_shape, max_partitions, pa_decode, pa_decode_partitions,
     pa_decode_partitions_debug, pa_decode_partitions_timed, pa_decode_v1, pa_decode_v2, pa_lse_reduce,
-    pa_lse_reduce_timed, status_string,
+    pa_lse_reduce_timed, pa_prefill, status_string,
 )

@@ -55,6 +55,8 @@ _SIGS = {
     "pa_decode_partitions_timed": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_float,
                                                   _P, _P, _P, ctypes.c_int, _P, _P, _P]),
     "pa_lse_reduce_timed": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_int, _P, _P, _P]),
+    "pa_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_int32,
+                                  ctypes.c_int32, ctypes.c_float, _P]),
     "pa_max_partitions": (ctypes.c_int64, [ctypes.POINTER(PaShape)]),
     "pa_partials_elems": (ctypes.c_int64, [ctypes.POINTER(PaShape), ctypes.c_int]),
     "pa_check_args": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), _P, _P, _P, ctypes.c_int]),
@@ -249,6 +251,26 @@ def pa_lse_reduce_timed(out, exp_sums, max_logits, tmp_out, seq_lens, shape: PaS
     _call("pa_lse_reduce_timed", load().pa_lse_reduce_timed(
         _ptr(out), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), _ptr(seq_lens), ctypes.byref(shape),
         int(mode), ctypes.c_void_p(start_event), ctypes.c_void_p(stop_event), _stream(stream, out.device)))
+
+
+def pa_prefill(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, scale, max_query_len,
+               stream=None):
+    """Prefix/chunked prefill over the paged cache: q, out [T, H, D] packed by token."""
+    _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens)
+    import torch
+    if not query_start_loc.is_cuda or query_start_loc.dtype != torch.int32 or not query_start_loc.is_contiguous():
+        raise PaError(PA_EINVAL, "query_start_loc must be a contiguous int32 GPU tensor")
+    if query_start_loc.numel() != block_tables.shape[0] + 1:
+        raise PaError(PA_EINVAL, "query_start_loc must hold num_seqs + 1 entries")
+    T, H, D = q.shape
+    NB, Hkv, BS, D2 = k_cache.shape
+    if D2 != D:
+        raise PaError(PA_EINVAL, f"head_dim of q ({D}) and cache ({D2}) differ")
+    sh = PaShape(block_tables.shape[0], H, Hkv, D, BS, block_tables.shape[1], NB, _dtype_code(q.dtype), 0)
+    _call("pa_prefill", load().pa_prefill(
+        _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
+        _ptr(query_start_loc), ctypes.byref(sh), int(T), int(max_query_len), float(scale),
+        _stream(stream, q.device)))
 
 
 class HipEvents:

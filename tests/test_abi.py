@@ -158,3 +158,30 @@ def test_status_strings(lib):
 def test_library_missing_fails_loudly(tmp_path):
     with pytest.raises(RuntimeError, match="missing"):
         L.load(str(tmp_path / "nope.so"))
+
+
+def test_prefill_validation(lib):
+    a = ctypes.c_void_p(A)
+    n = None
+
+    def call(sh, T=10, maxq=5, **ptrs):
+        p = dict(out=A, q=A, k=A, v=A, bt=A, sl=A, qsl=A)
+        p.update(ptrs)
+        c = lambda x: None if x is None else ctypes.c_void_p(x)
+        # validation fails before any launch, so these fake addresses are never touched
+        return lib.pa_prefill(c(p["out"]), c(p["q"]), c(p["k"]), c(p["v"]), c(p["bt"]), c(p["sl"]), c(p["qsl"]),
+                              ctypes.byref(sh), T, maxq, ctypes.c_float(1.0), n)
+
+    assert call(shape(dtype=L.PA_F32)) == L.PA_EUNSUPPORTED
+    assert call(shape(head_dim=64)) == L.PA_EUNSUPPORTED
+    assert call(shape(num_heads=15)) == L.PA_EINVAL
+    for name in ("out", "q", "k", "v", "bt", "sl", "qsl"):
+        assert call(shape(), **{name: None}) == L.PA_EINVAL, name
+    assert call(shape(), q=A + 8) == L.PA_EALIGN
+    assert call(shape(), qsl=A + 2) == L.PA_EALIGN
+    assert call(shape(), T=-1) == L.PA_EINVAL
+    assert call(shape(), maxq=-3) == L.PA_EINVAL
+    assert call(shape(num_seqs=1 << 30, num_heads=16, num_kv_heads=16), maxq=1 << 30) == L.PA_EUNSUPPORTED
+    # empty work: nothing to read, every pointer may be NULL (nothing is launched on the null stream)
+    assert lib.pa_prefill(n, n, n, n, n, n, n, ctypes.byref(shape(num_seqs=0)), 0, 0, ctypes.c_float(1.0), n) == L.PA_OK
+    assert a is not None
