@@ -917,7 +917,7 @@ struct PrefillParams {
   float scale2;
 };
 
-template <typename T, int D, int NW, int NTW, int TB>
+template <typename T, int D, int NW, int NTW, int TB, bool PF>
 __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   typedef typename H16<T>::x8 tx8;
   typedef typename H16<T>::x4 tx4;
@@ -1019,8 +1019,9 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     ids = id;
   };
 
-  BTile<D, TB> tl;
-  for (int t = 0; t < ntiles; ++t) {
+  // Issues tile t's loads (tiles are issued in order, so the id list is
+  // refilled exactly when a new CH-tile chunk starts).
+  auto issue = [&](BTile<D, TB>& tl, int t) {
     if (t % CH == 0) refill(t / CH);
     int64_t phys[TB];
     bool vb[TB];
@@ -1030,6 +1031,9 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
       phys[b] = __builtin_amdgcn_readlane(ids, (t % CH) * TB + b);
     }
     issue_tile<T, D, TB, false>(tl, kbase, vbase, block_elems, phys, vb, g, grp);
+  };
+
+  auto compute = [&](BTile<D, TB>& tl, int t) {
 
     // K: registers -> swizzled LDS tile -> MFMA A operands.
 #pragma unroll
@@ -1147,6 +1151,29 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
             acc[jj][h * 8 + j] = H16<T>::mma16(__builtin_bit_cast(tx4, a), pv4, acc[jj][h * 8 + j]);
           }
       }
+    }
+  };
+
+  BTile<D, TB> A;
+  issue(A, 0);
+  if constexpr (PF) {
+    // Two register stages: the next tile's loads are in flight while this
+    // tile's math runs (a workgroup's waves are few per SIMD here).
+    BTile<D, TB> B;
+    for (int t = 0;;) {
+      if (t + 1 < ntiles) issue(B, t + 1);
+      compute(A, t);
+      if (t + 1 >= ntiles) break;
+      if (t + 2 < ntiles) issue(A, t + 2);
+      compute(B, t + 1);
+      if (t + 2 >= ntiles) break;
+      t += 2;
+    }
+  } else {
+    for (int t = 0;;) {
+      compute(A, t);
+      if (++t >= ntiles) break;
+      issue(A, t);
     }
   }
 
@@ -1381,22 +1408,33 @@ hipError_t launch_reduce(const ReduceParams& R, int dtype, const Launch& L) {
   return launch_reduce_t<float>(R, L);
 }
 
-// Prefill launch shape: 128 query rows per workgroup (QT tokens x G heads),
-// D=128: 4 waves x 2 N-tiles; D=256: 8 waves x 1 N-tile (register budget).
+// Prefill launch shape: 128 query rows per workgroup (QT tokens x G heads).
+// D=128, at most kPrefillSmallGrid workgroups (one or two per CU, long
+// contexts): 8 waves x 1 N-tile, two-block tiles, next tile prefetched into
+// registers, since few waves share a SIMD; larger grids: 4 waves x 2 N-tiles,
+// one-block tiles, no prefetch (2 waves per SIMD resident). D=256: 8 waves x 1
+// N-tile, one-block tiles (register budget). Measured on the four prefill
+// workloads against the other combinations of these knobs.
 constexpr int kPrefillRows = 128;
+constexpr int64_t kPrefillSmallGrid = 512;
 
 template <typename T>
 hipError_t launch_prefill_t(const PrefillParams& P, int D, int nqt, const Launch& L) {
   const dim3 grid((unsigned)((int64_t)P.S * P.Hkv * nqt));
   if (grid.x == 0) return nothing_launched(L);
   if (D == 128) {
+    if ((int64_t)grid.x <= kPrefillSmallGrid) {
+      constexpr int NW = 8, NTW = 1, TB = 2;
+      const size_t smem = (size_t)NW * TB * 16 * 128 * sizeof(T);
+      return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true>, grid, dim3(NW * 64), smem, L, P);
+    }
     constexpr int NW = 4, NTW = 2, TB = 1;
     const size_t smem = (size_t)NW * TB * 16 * 128 * sizeof(T);
-    return launch(pa_prefill_h16<T, 128, NW, NTW, TB>, grid, dim3(NW * 64), smem, L, P);
+    return launch(pa_prefill_h16<T, 128, NW, NTW, TB, false>, grid, dim3(NW * 64), smem, L, P);
   }
   constexpr int NW = 8, NTW = 1, TB = 1;
   const size_t smem = (size_t)NW * TB * 16 * 256 * sizeof(T);
-  return launch(pa_prefill_h16<T, 256, NW, NTW, TB>, grid, dim3(NW * 64), smem, L, P);
+  return launch(pa_prefill_h16<T, 256, NW, NTW, TB, false>, grid, dim3(NW * 64), smem, L, P);
 }
 
 int check_prefill(const void* out, const void* q, const void* k, const void* v, const int32_t* bt,

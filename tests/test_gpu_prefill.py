@@ -189,3 +189,14 @@ def test_prefill_rejects_f32(dev):
     x = W.make_prefill_inputs(cfg, seed=57, context_lens=[3], query_lens=[2])
     with pytest.raises(pa.PaError):
         run(x, dev)
+
+
+def test_prefill_large_grid_every_token(dev):
+    """More than 512 workgroups (the many-workgroup launch shape), every token compared."""
+    rng = np.random.default_rng(58)
+    S = 40
+    ctx = rng.integers(0, 300, size=S)
+    ql = rng.integers(100, 129, size=S)
+    x = W.make_prefill_inputs(W.PREFILL_CONFIGS[2], seed=58, context_lens=ctx, query_lens=ql)
+    say(f"prefill large grid: {S} seqs, {x.num_query_tokens} tokens")
+    check_all(x, run(x, dev), "large grid")
