@@ -402,6 +402,73 @@ def prefill_to_device(x: PrefillInputs, device="cuda"):
     return d
 
 
+# ---------------------------------------------------------------- MoE routing
+@dataclass(frozen=True)
+class MoeConfig:
+    """One MoE routing workload: T tokens, E experts, top k, hidden size."""
+    name: str
+    num_tokens: int
+    num_experts: int
+    top_k: int
+    hidden: int
+    dtype: str = "bf16"          # hidden rows and expert outputs
+    renormalize: bool = True
+
+
+# 256 experts with top 8 (the pages' MoE rewrite); 16384 tokens is the
+# prefill batch the same passage sizes; 256 tokens a decode step at 256
+# concurrent sequences. Hidden size 2048 is a stand-in (the pages give none).
+MOE_CONFIGS = {
+    1: MoeConfig("prefill-T16384-E256-k8-H2048-bf16", 16384, 256, 8, 2048),
+    2: MoeConfig("decode-T256-E256-k8-H2048-bf16", 256, 256, 8, 2048),
+}
+
+
+@dataclass
+class MoeInputs:
+    cfg: MoeConfig
+    seed: int
+    logits: np.ndarray      # float32 [T, E] router logits
+    x: np.ndarray           # [T, Hd] hidden rows (uint16 bf16 bits / float16 / float32)
+    y_sorted: np.ndarray    # [T*K, Hd] stand-in expert outputs, in sorted-pair order
+
+
+def make_moe_inputs(cfg: MoeConfig | int, seed: int | None = None, *, num_tokens: int | None = None) -> MoeInputs:
+    """Router logits N(0, 1) in fp32, hidden rows and stand-in expert outputs
+    N(0, 1) rounded to the dtype (purposes 1, 2, 3 of the seed)."""
+    number = None
+    if isinstance(cfg, int):
+        number = cfg
+        cfg = MOE_CONFIGS[cfg]
+    if num_tokens is not None:
+        cfg = MoeConfig(cfg.name + "-custom", int(num_tokens), cfg.num_experts, cfg.top_k, cfg.hidden,
+                        cfg.dtype, cfg.renormalize)
+    if seed is None:
+        seed = 3000 + (number if number is not None else 0)
+    T, E, K, Hd = cfg.num_tokens, cfg.num_experts, cfg.top_k, cfg.hidden
+    store = {"f32": np.float32, "f16": np.float16, "bf16": np.uint16}[cfg.dtype]
+    logits = np.empty((T, E), dtype=np.float32)
+    _fill_normal(logits.reshape(-1), seed, 1, "f32")
+    x = np.empty((T, Hd), dtype=store)
+    _fill_normal(x.reshape(-1), seed, 2, cfg.dtype)
+    y = np.empty((T * K, Hd), dtype=store)
+    _fill_normal(y.reshape(-1), seed, 3, cfg.dtype)
+    return MoeInputs(cfg, seed, logits, x, y)
+
+
+def moe_bytes(cfg: MoeConfig) -> dict:
+    """Algorithmic bytes of each routing step (elem = bytes per hidden value)."""
+    T, E, K, Hd = cfg.num_tokens, cfg.num_experts, cfg.top_k, cfg.hidden
+    e = {"f32": 4, "f16": 2, "bf16": 2}[cfg.dtype]
+    N = T * K
+    return {
+        "topk_softmax": T * E * 4 + N * 8,               # logits in; weights + ids out
+        "sort_by_expert": N * 4 + N * 8 + (E + 1) * 4,   # ids in; sorted pairs, positions, offsets out
+        "permute": N * 4 + 2 * N * Hd * e,               # pair list; rows gathered and written
+        "combine": N * (4 + 4) + N * Hd * e + T * Hd * e,  # positions, weights; expert rows in; out rows
+    }
+
+
 def algorithmic_bytes(seq_lens, num_heads: int, num_kv_heads: int, head_dim: int, elem_bytes: int) -> int:
     """Bytes the decode step must move at minimum.
 

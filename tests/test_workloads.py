@@ -132,3 +132,16 @@ def test_prefill_overrides_and_flops():
     assert W.prefill_flops(x.seq_lens, x.query_lens, 16, 128) == 4 * 128 * 16 * keys
     p = W.make_prefill_inputs(W.PREFILL_CONFIGS[2], seed=5, context_lens=[3], query_lens=[20], poison=True)
     assert p.k_cache.shape[0] == p.num_blocks and p.extra["poison_block"] == p.num_blocks - 1
+
+
+def test_moe_inputs_shapes_and_bytes():
+    x = W.make_moe_inputs(2)
+    c = x.cfg
+    assert x.logits.shape == (256, 256) and x.logits.dtype == np.float32
+    assert x.x.shape == (256, 2048) and x.y_sorted.shape == (256 * 8, 2048)
+    y = W.make_moe_inputs(2)
+    assert np.array_equal(x.logits, y.logits) and np.array_equal(x.y_sorted, y.y_sorted)
+    b = W.moe_bytes(c)
+    assert b["permute"] == 256 * 8 * 4 + 2 * 256 * 8 * 2048 * 2
+    small = W.make_moe_inputs(1, num_tokens=10)
+    assert small.x.shape == (10, 2048)
