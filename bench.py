@@ -400,6 +400,121 @@ def bench_prefill(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: fl
     return res
 
 
+def moe_cpu_baseline(x, budget_s: float) -> dict:
+    """The oracle's routing steps on the host, over as many tokens as fit the budget."""
+    import oracle.moe as om
+    from paged_attention_decode_06_amd import workloads as W
+    c = x.cfg
+    T = c.num_tokens
+    y = W.bf16_bits_to_f32(x.y_sorted).astype(np.float64) if c.dtype == "bf16" else x.y_sorted.astype(np.float64)
+    t0 = time.perf_counter()
+    n = 0
+    nbytes = 0
+    per = W.moe_bytes(c)
+    while True:
+        w, ids = om.topk_softmax(x.logits, c.top_k, c.renormalize)
+        sp, pp, off = om.sort_by_expert(ids, c.num_experts)
+        om.permute_rows(x.x, sp, c.top_k)
+        om.combine(y, w, pp)
+        n += 1
+        nbytes += sum(per.values())
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    el = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count() or 1
+    return {"value": round(nbytes / el / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"NumPy oracle, {n} full routing passes over {T} tokens in {el:.1f} s",
+            "seconds": round(el, 3)}
+
+
+def bench_moe(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float, dev) -> dict:
+    """MoE routing: topk softmax, sort by expert (3 launches), permute, combine per step."""
+    import torch
+
+    import paged_attention_decode_06_amd as pa
+    from paged_attention_decode_06_amd import workloads as W
+
+    x = W.make_moe_inputs(num)
+    c = x.cfg
+    T, E, K, Hd = c.num_tokens, c.num_experts, c.top_k, c.hidden
+    bf = lambda a: torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    logits = torch.from_numpy(x.logits).to(dev)
+    xh, ys = bf(x.x), bf(x.y_sorted)
+    w = torch.empty((T, K), dtype=torch.float32, device=dev)
+    ids = torch.empty((T, K), dtype=torch.int32, device=dev)
+    sp = torch.empty((T * K,), dtype=torch.int32, device=dev)
+    pp = torch.empty_like(sp)
+    off = torch.empty((E + 1,), dtype=torch.int32, device=dev)
+    ws = torch.empty((pa.moe_sort_workspace_bytes(T, E, K) // 4,), dtype=torch.int32, device=dev)
+    xs = torch.empty((T * K, Hd), dtype=torch.bfloat16, device=dev)
+    out = torch.empty((T, Hd), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    scrub_buf = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.empty((), dtype=torch.float32, device=dev)
+    stages = [
+        ("topk_softmax", lambda: pa.pa_moe_topk_softmax(w, ids, logits, c.renormalize, stream=stream)),
+        ("sort_by_expert", lambda: pa.pa_moe_sort_by_expert(sp, pp, off, ids, E, ws, stream=stream)),
+        ("permute", lambda: pa.pa_moe_permute(xs, xh, sp, K, stream=stream)),
+        ("combine", lambda: pa.pa_moe_combine(out, ys, w, pp, stream=stream)),
+    ]
+    for _ in range(warmup):
+        for _, f in stages:
+            f()
+    torch.cuda.synchronize(dev)
+    # whole step, events around the four stages
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        if scrub:
+            torch.sum(scrub_buf, dim=None, out=sink)
+        ev[i][0].record(stream)
+        for _, f in stages:
+            f()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    # per stage, events around each (markers add a few us per stage)
+    per = {name: [] for name, _ in stages}
+    for i in range(steps):
+        if scrub:
+            torch.sum(scrub_buf, dim=None, out=sink)
+        marks = []
+        for name, f in stages:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record(stream); f(); b.record(stream)
+            marks.append((name, a, b))
+        torch.cuda.synchronize(dev)
+        for name, a, b in marks:
+            per[name].append(a.elapsed_time(b))
+    per_us = {k: round(float(np.mean(v)) * 1e3, 2) for k, v in per.items()}
+    nbytes = W.moe_bytes(c)
+    t = float(ms.mean())
+    total = sum(nbytes.values())
+    gbs = total / (t * 1e-3) / 1e9
+    pk = nbytes["permute"] / (per_us["permute"] * 1e-6) / 1e9
+    res = {
+        "metric": "MoE routing path (topk softmax, sort by expert, permute, combine) achieved HBM GB/s",
+        "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": round(t, 5), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": c.dtype, "data": "synthetic",
+        "config": {"workload": c.name, "num_tokens": T, "num_experts": E, "top_k": K, "hidden": Hd,
+                   "renormalize": c.renormalize, "seed": x.seed,
+                   "note": "expert GEMMs not included; y_sorted is a seeded stand-in for their outputs"},
+        "us_per_step_p10_p50_p90": [round(float(np.percentile(ms, q_)) * 1e3, 2) for q_ in (10, 50, 90)],
+        "stage_us_mean": per_us,
+        "algorithmic_bytes": nbytes,
+        "tokens_per_s": round(T / (t * 1e-3), 1),
+        "roofline": {"bound": "hbm", "achieved": round(pk, 2), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(pk / PEAK_GBS, 4), "traffic": None, "kernel": "pa_moe_permute",
+                     "algorithmic_bytes_per_launch": int(nbytes["permute"])},
+    }
+    res["cpu_baseline"] = moe_cpu_baseline(x, cpu_budget) if cpu_budget > 0 else None
+    del scrub_buf
+    return res
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -416,6 +531,9 @@ def main(argv=None):
     ap.add_argument("--prefill", type=int, default=0, metavar="N",
                     help="measure prefix/chunked-prefill workload N (1..4; 0 = decode); --all-prefill for all")
     ap.add_argument("--all-prefill", action="store_true", help="every prefill workload, one JSON line each")
+    ap.add_argument("--moe", type=int, default=0, metavar="N",
+                    help="measure MoE routing workload N (1: 16384 tokens, 2: 256 tokens); --all-moe for both")
+    ap.add_argument("--all-moe", action="store_true", help="every MoE routing workload, one JSON line each")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args(argv)
@@ -442,6 +560,11 @@ def main(argv=None):
         return 0
     import paged_attention_decode_06_amd as pa
     pa.load()
+    if args.moe or args.all_moe:
+        for n in ([1, 2] if args.all_moe else [args.moe]):
+            res = bench_moe(n, args.steps, args.warmup, not args.no_scrub, args.cpu_budget, dev)
+            print(json.dumps(res), flush=True)
+        return 0
     if args.prefill or args.all_prefill:
         for n in ([1, 2, 3, 4] if args.all_prefill else [args.prefill]):
             res = bench_prefill(n, args.steps, args.warmup, not args.no_scrub, args.cpu_budget, dev)

@@ -1,6 +1,8 @@
 """Paged-attention decode for MI355X (gfx950).
 
-The compute path is the HIP library libpa_decode.so (include/pa_decode.h);
+The compute path is the HIP library libpa_decode.so (include/pa_decode.h:
+decode and prefill attention over the paged cache; include/pa_moe.h: the MoE
+routing path);
 this package is its thin ctypes binding plus the seeded input generators
 (`workloads`). Build the library with `python -m paged_attention_decode_06_amd._build`.
 """
@@ -9,4 +11,5 @@ from ._lib import (  # noqa: F401
     PaError, PaShape, alloc_partials, load, make_shape, max_partitions, pa_decode, pa_decode_partitions,
     pa_decode_partitions_debug, pa_decode_partitions_timed, pa_decode_v1, pa_decode_v2, pa_lse_reduce,
     pa_lse_reduce_timed, pa_prefill, status_string,
+    pa_moe_topk_softmax, moe_sort_workspace_bytes, pa_moe_sort_by_expert, pa_moe_permute, pa_moe_combine,
 )

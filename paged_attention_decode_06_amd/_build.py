@@ -8,6 +8,7 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "pa_decode.hip")
+SOURCES = [SRC, os.path.join(HERE, "csrc", "pa_moe.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpa_decode.so")
 ARCH = "gfx950"
@@ -28,7 +29,7 @@ def hipcc() -> str:
 def build(verbose: bool = False, extra_flags: list[str] | None = None, out: str = LIB) -> str:
     """Build libpa_decode.so next to this file and return its path."""
     tmp = out + ".tmp"
-    cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [hipcc(), *HIP_FLAGS, *(extra_flags or []), "-I", INCLUDE, *SOURCES, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     msgs = [l for l in (res.stdout + res.stderr).splitlines()
             if "packed-fp32-ops" not in l and "is not a recognized feature" not in l]

@@ -13,6 +13,7 @@ import re
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpa_decode.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "pa_decode.h")
+HEADERS = [HEADER, os.path.join(os.path.dirname(HERE), "include", "pa_moe.h")]
 
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 MODE_AUTO, MODE_V1, MODE_V2 = 0, 1, 2
@@ -58,6 +59,15 @@ _SIGS = {
     "pa_prefill": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_int32,
                                   ctypes.c_int32, ctypes.c_float, _P]),
     "pa_max_partitions": (ctypes.c_int64, [ctypes.POINTER(PaShape)]),
+    "pa_moe_topk_softmax": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int, _P]),
+    "pa_moe_sort_workspace_bytes": (ctypes.c_int64, [ctypes.c_int32, ctypes.c_int32, ctypes.c_int32]),
+    "pa_moe_sort_by_expert": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P,
+                                             ctypes.c_int64, _P]),
+    "pa_moe_permute": (ctypes.c_int, [_P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      _P]),
+    "pa_moe_combine": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                      ctypes.c_int32, _P]),
     "pa_partials_elems": (ctypes.c_int64, [ctypes.POINTER(PaShape), ctypes.c_int]),
     "pa_check_args": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), _P, _P, _P, ctypes.c_int]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -65,11 +75,14 @@ _SIGS = {
 }
 
 
-def header_functions(path: str = HEADER) -> list[str]:
-    """Names of the functions include/pa_decode.h declares."""
-    text = open(path).read()
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text)))
+def header_functions(paths=None) -> list[str]:
+    """Names of the functions the library's headers (include/*.h) declare."""
+    names = set()
+    for path in (paths or HEADERS):
+        text = open(path).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names.update(re.findall(r"\b(pa_[a-z0-9_]+)\s*\(", text))
+    return sorted(names)
 
 
 def load(path: str | None = None) -> ctypes.CDLL:
@@ -271,6 +284,71 @@ def pa_prefill(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
         _ptr(query_start_loc), ctypes.byref(sh), int(T), int(max_query_len), float(scale),
         _stream(stream, q.device)))
+
+
+# ---------------------------------------------------------------- MoE routing
+def _gpu_contig(*ts):
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise PaError(PA_EINVAL, "MoE tensors must be contiguous GPU tensors")
+
+
+def pa_moe_topk_softmax(topk_weights, topk_ids, logits, renormalize=True, stream=None):
+    """logits float32 [T, E] -> topk_weights float32 [T, K], topk_ids int32 [T, K]."""
+    import torch
+    _gpu_contig(topk_weights, topk_ids, logits)
+    if logits.dtype != torch.float32 or topk_weights.dtype != torch.float32 or topk_ids.dtype != torch.int32:
+        raise PaError(PA_EINVAL, "logits/weights float32, ids int32")
+    T, E = logits.shape
+    K = topk_ids.shape[1]
+    if tuple(topk_weights.shape) != (T, K) or topk_ids.shape[0] != T:
+        raise PaError(PA_EINVAL, "weights and ids must be [T, K]")
+    _call("pa_moe_topk_softmax", load().pa_moe_topk_softmax(
+        _ptr(topk_weights), _ptr(topk_ids), _ptr(logits), T, E, K, int(bool(renormalize)),
+        _stream(stream, logits.device)))
+
+
+def moe_sort_workspace_bytes(T: int, E: int, K: int) -> int:
+    r = int(load().pa_moe_sort_workspace_bytes(T, E, K))
+    _call("pa_moe_sort_workspace_bytes", r if r < 0 else 0)
+    return r
+
+
+def pa_moe_sort_by_expert(sorted_pairs, pair_pos, expert_offsets, topk_ids, num_experts, workspace, stream=None):
+    """topk_ids int32 [T, K] -> sorted_pairs, pair_pos int32 [T*K], expert_offsets int32 [E+1]."""
+    import torch
+    _gpu_contig(sorted_pairs, pair_pos, expert_offsets, topk_ids, workspace)
+    for t in (sorted_pairs, pair_pos, expert_offsets, topk_ids):
+        if t.dtype != torch.int32:
+            raise PaError(PA_EINVAL, "sort arrays must be int32")
+    T, K = topk_ids.shape
+    if sorted_pairs.numel() != T * K or pair_pos.numel() != T * K or expert_offsets.numel() != num_experts + 1:
+        raise PaError(PA_EINVAL, "sorted_pairs/pair_pos need T*K entries, expert_offsets E+1")
+    nbytes = workspace.numel() * workspace.element_size()
+    _call("pa_moe_sort_by_expert", load().pa_moe_sort_by_expert(
+        _ptr(sorted_pairs), _ptr(pair_pos), _ptr(expert_offsets), _ptr(topk_ids), T, int(num_experts), K,
+        _ptr(workspace), int(nbytes), _stream(stream, topk_ids.device)))
+
+
+def pa_moe_permute(x_sorted, x, sorted_pairs, top_k, stream=None):
+    """x [T, hidden] -> x_sorted [T*K, hidden]: row i = x[sorted_pairs[i] // K]."""
+    _gpu_contig(x_sorted, x, sorted_pairs)
+    T, Hd = x.shape
+    if tuple(x_sorted.shape) != (T * top_k, Hd) or x_sorted.dtype != x.dtype or sorted_pairs.numel() != T * top_k:
+        raise PaError(PA_EINVAL, "x_sorted must be [T*K, hidden] of x's dtype; sorted_pairs T*K entries")
+    _call("pa_moe_permute", load().pa_moe_permute(_ptr(x_sorted), _ptr(x), _ptr(sorted_pairs), T, int(top_k), Hd,
+                                                  _dtype_code(x.dtype), _stream(stream, x.device)))
+
+
+def pa_moe_combine(out, y_sorted, topk_weights, pair_pos, stream=None):
+    """out[t] = sum_j topk_weights[t, j] * y_sorted[pair_pos[t*K + j]] (fp32 accumulation, order j)."""
+    _gpu_contig(out, y_sorted, topk_weights, pair_pos)
+    T, K = topk_weights.shape
+    Hd = out.shape[1]
+    if tuple(y_sorted.shape) != (T * K, Hd) or y_sorted.dtype != out.dtype or pair_pos.numel() != T * K:
+        raise PaError(PA_EINVAL, "y_sorted must be [T*K, hidden] of out's dtype; pair_pos T*K entries")
+    _call("pa_moe_combine", load().pa_moe_combine(_ptr(out), _ptr(y_sorted), _ptr(topk_weights), _ptr(pair_pos), T, K,
+                                                  Hd, _dtype_code(out.dtype), _stream(stream, out.device)))
 
 
 class HipEvents:

@@ -1,0 +1,433 @@
+// MoE routing path for gfx950 (MI355X): router top-k softmax, stable sort of
+// the token-expert pairs by expert, gather of the expert inputs into sorted
+// order, and the weighted scatter-back of the expert outputs.
+//
+// Method (project_6 commit cd0d9e1a, qwen3_6_scripts, the MoE prefill
+// rewrite; project_6 commit 490ff98a, Dockerfile, topk_softmax): flatten the
+// T x K assignments, sort them by expert so every expert's rows are
+// contiguous, and add the weighted expert outputs back in one pass. The
+// expert GEMMs between permute and combine are not part of this file.
+//
+// Design (wave64):
+//   * top-k softmax: one wave per token, E/64 logits per lane; max and sum by
+//     xor trees, then K rounds of a wave-wide argmax on (logit, -id) with a
+//     per-lane bitmask of experts already taken.
+//   * sort: a stable counting sort in three launches. Chunks of 1024 pairs:
+//     every pair's rank among the earlier same-expert pairs of its chunk (LDS
+//     scan) and the chunk's per-expert counts; one workgroup turns the
+//     [chunk][expert] counts into write bases (a prefix over chunks per expert
+//     plus the expert offsets); then every pair lands at base + rank.
+//   * permute and combine: one wave per row, 16-byte loads and stores; the
+//     combine gathers each token's K rows (no atomics) and sums them in fp32
+//     in the order j = 0..K-1.
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pa_decode.h"
+#include "pa_moe.h"
+
+namespace {
+
+constexpr int kSortChunk = 1024;   // pairs per counting-sort chunk (one thread each)
+constexpr int kThreads = 256;
+constexpr float kLog2e = 1.4426950408889634f;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
+
+// ---------------------------------------------------------------- top-k softmax
+template <int VPL>
+__global__ __launch_bounds__(kThreads) void moe_topk_softmax_kernel(float* __restrict__ w_out,
+                                                                    int32_t* __restrict__ id_out,
+                                                                    const float* __restrict__ logits, int T,
+                                                                    int E, int K, int renorm) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const float* row = logits + (int64_t)t * E;
+  float v[VPL];
+#pragma unroll
+  for (int u = 0; u < VPL; ++u) {
+    const int e = lane + 64 * u;
+    v[u] = e < E ? row[e] : -INFINITY;
+  }
+  float m = v[0];
+#pragma unroll
+  for (int u = 1; u < VPL; ++u) m = fmaxf(m, v[u]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
+  float sum = 0.f;
+#pragma unroll
+  for (int u = 0; u < VPL; ++u)
+    if (lane + 64 * u < E) sum += __builtin_amdgcn_exp2f((v[u] - m) * kLog2e);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+
+  uint32_t taken = 0;  // bit u: expert lane + 64u already chosen
+  float my_w = 0.f;
+  int my_id = 0;
+  for (int j = 0; j < K; ++j) {
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int u = 0; u < VPL; ++u) {
+      const int e = lane + 64 * u;
+      if (e < E && !((taken >> u) & 1u) && (v[u] > bv || (v[u] == bv && e < bi))) {
+        bv = v[u];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float ov = __shfl_xor(bv, o);
+      const int oi = __shfl_xor(bi, o);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (bi >= E) {  // only NaN logits left: a data error, kept in range
+      bi = 0;
+      bv = -INFINITY;
+    } else if ((bi & 63) == lane) {
+      taken |= 1u << (bi >> 6);
+    }
+    if (lane == j) {
+      my_w = (bv > -INFINITY) ? __builtin_amdgcn_exp2f((bv - m) * kLog2e) / sum : 0.f;
+      my_id = bi;
+    }
+  }
+  if (renorm) {
+    float s = lane < K ? my_w : 0.f;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    if (s > 0.f) my_w /= s;
+  }
+  if (lane < K) {
+    w_out[(int64_t)t * K + lane] = my_w;
+    id_out[(int64_t)t * K + lane] = my_id;
+  }
+}
+
+// ---------------------------------------------------------------- stable counting sort
+// Phase 1: per chunk, each pair's rank among the earlier pairs of the chunk
+// with the same expert, and the chunk's per-expert counts.
+__global__ __launch_bounds__(kSortChunk) void moe_sort_count_kernel(const int32_t* __restrict__ ids, int N, int E,
+                                                                  int32_t* __restrict__ counts,
+                                                                  int32_t* __restrict__ rank) {
+  __shared__ int32_t sid[kSortChunk];
+  __shared__ int32_t scnt[PA_MOE_MAX_EXPERTS];
+  const int c = blockIdx.x;
+  const int base = c * kSortChunk;
+  const int n = min(kSortChunk, N - base);
+  const int i = threadIdx.x;
+  if (i < E) scnt[i] = 0;
+  sid[i] = i < n ? clampi(ids[base + i], 0, E - 1) : -1;
+  __syncthreads();
+  if (i < n) {
+    const int e = sid[i];
+    int r = 0;
+#pragma unroll 8
+    for (int j = 0; j < i; ++j) r += (sid[j] == e);
+    rank[base + i] = r;
+    atomicAdd(&scnt[e], 1);
+  }
+  __syncthreads();
+  if (i < E) counts[(int64_t)c * E + i] = scnt[i];
+}
+
+// Phase 2 (one workgroup, one thread per expert): counts[c][e] becomes the
+// sorted position where chunk c's first pair of expert e lands.
+__global__ __launch_bounds__(PA_MOE_MAX_EXPERTS) void moe_sort_scan_kernel(int32_t* __restrict__ counts, int NC,
+                                                                           int E, int N,
+                                                                           int32_t* __restrict__ offsets) {
+  __shared__ int32_t tot[PA_MOE_MAX_EXPERTS];
+  const int e = threadIdx.x;
+  int run = 0;
+  if (e < E) {
+#pragma unroll 8
+    for (int c = 0; c < NC; ++c) {
+      const int x = counts[(int64_t)c * E + e];
+      counts[(int64_t)c * E + e] = run;
+      run += x;
+    }
+  }
+  tot[e] = e < E ? run : 0;
+  __syncthreads();
+  // exclusive prefix over experts (Hillis-Steele on an inclusive copy)
+  for (int d = 1; d < PA_MOE_MAX_EXPERTS; d <<= 1) {
+    const int add = e >= d ? tot[e - d] : 0;
+    __syncthreads();
+    tot[e] += add;
+    __syncthreads();
+  }
+  const int start = tot[e] - (e < E ? run : 0);
+  if (e < E) {
+    offsets[e] = start;
+#pragma unroll 8
+    for (int c = 0; c < NC; ++c) counts[(int64_t)c * E + e] += start;
+  }
+  if (e == 0) offsets[E] = N;
+}
+
+// Phase 3: every pair lands at its chunk's base for its expert plus its rank.
+__global__ __launch_bounds__(kSortChunk) void moe_sort_scatter_kernel(const int32_t* __restrict__ ids, int N, int E,
+                                                                    const int32_t* __restrict__ counts,
+                                                                    const int32_t* __restrict__ rank,
+                                                                    int32_t* __restrict__ sorted_pairs,
+                                                                    int32_t* __restrict__ pair_pos) {
+  const int c = blockIdx.x;
+  const int base = c * kSortChunk;
+  const int n = min(kSortChunk, N - base);
+  const int i = threadIdx.x;
+  if (i < n) {
+    const int a = base + i;
+    const int e = clampi(ids[a], 0, E - 1);
+    const int pos = counts[(int64_t)c * E + e] + rank[a];
+    sorted_pairs[pos] = a;
+    pair_pos[a] = pos;
+  }
+}
+
+// ---------------------------------------------------------------- permute / combine
+__global__ __launch_bounds__(kThreads) void moe_permute_kernel(char* __restrict__ dst, const char* __restrict__ src,
+                                                               const int32_t* __restrict__ sorted_pairs, int N,
+                                                               int K, int64_t row_bytes) {
+  const int lane = threadIdx.x & 63;
+  const int i = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (i >= N) return;
+  const int a = clampi(sorted_pairs[i], 0, N - 1);
+  const char* s = src + (int64_t)(a / K) * row_bytes;
+  char* d = dst + (int64_t)i * row_bytes;
+  for (int64_t off = (int64_t)lane * 16; off < row_bytes; off += 64 * 16)
+    *reinterpret_cast<u32x4*>(d + off) = *reinterpret_cast<const u32x4*>(s + off);
+}
+
+template <typename E>
+struct Row16;  // 16 raw bytes of a row <-> floats
+template <>
+struct Row16<float> {
+  static constexpr int n = 4;
+  typedef float f4 __attribute__((ext_vector_type(4)));
+  static __device__ __forceinline__ void unpack(float (&f)[8], u32x4 x) {
+    const f4 v = __builtin_bit_cast(f4, x);  // whole-vector casts only
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f[i] = v[i];
+  }
+  static __device__ __forceinline__ u32x4 pack(const float (&f)[8]) {
+    const f4 v = {f[0], f[1], f[2], f[3]};
+    return __builtin_bit_cast(u32x4, v);
+  }
+};
+template <typename H>
+struct Row16Half {
+  static constexpr int n = 8;
+  typedef H h8 __attribute__((ext_vector_type(8)));
+  static __device__ __forceinline__ void unpack(float (&f)[8], u32x4 x) {
+    const h8 h = __builtin_bit_cast(h8, x);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) f[i] = (float)h[i];
+  }
+  static __device__ __forceinline__ u32x4 pack(const float (&f)[8]) {
+    h8 h;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) h[i] = (H)f[i];
+    return __builtin_bit_cast(u32x4, h);
+  }
+};
+template <>
+struct Row16<__bf16> : Row16Half<__bf16> {};
+template <>
+struct Row16<_Float16> : Row16Half<_Float16> {};
+
+// One wave per token. Each pass covers kCombineU 1 KB slices of the row and
+// issues the loads of up to 8 choices for all of them before any arithmetic,
+// so a wave keeps 16 loads of 16 bytes in flight; the sum still runs in the
+// order j = 0..K-1 for every element.
+constexpr int kCombineU = 2;
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void moe_combine_kernel(char* __restrict__ out, const char* __restrict__ y,
+                                                               const float* __restrict__ weights,
+                                                               const int32_t* __restrict__ pair_pos, int T, int K,
+                                                               int64_t row_bytes) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const int N = T * K;
+  // lane j < K holds choice j's weight and row; broadcast below in order j.
+  float wl = 0.f;
+  int pl = 0;
+  if (lane < K) {
+    wl = weights[(int64_t)t * K + lane];
+    pl = clampi(pair_pos[(int64_t)t * K + lane], 0, N - 1);
+  }
+  for (int64_t off0 = (int64_t)lane * 16; off0 < row_bytes; off0 += kCombineU * 64 * 16) {
+    float acc[kCombineU][8];
+#pragma unroll
+    for (int u = 0; u < kCombineU; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[u][i] = 0.f;
+    for (int j0 = 0; j0 < K; j0 += 8) {
+      u32x4 buf[8][kCombineU];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int pj = __shfl(pl, j0 + jj);
+#pragma unroll
+        for (int u = 0; u < kCombineU; ++u) {
+          const int64_t off = off0 + (int64_t)u * 64 * 16;
+          buf[jj][u] = (j0 + jj < K && off < row_bytes)
+                           ? *reinterpret_cast<const u32x4*>(y + (int64_t)pj * row_bytes + off)
+                           : (u32x4){0u, 0u, 0u, 0u};
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const float wj = __shfl(wl, j0 + jj);
+        if (j0 + jj < K) {
+#pragma unroll
+          for (int u = 0; u < kCombineU; ++u) {
+            float f[8];
+            Row16<E>::unpack(f, buf[jj][u]);
+#pragma unroll
+            for (int i = 0; i < Row16<E>::n; ++i) acc[u][i] += wj * f[i];
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kCombineU; ++u) {
+      const int64_t off = off0 + (int64_t)u * 64 * 16;
+      if (off < row_bytes) *reinterpret_cast<u32x4*>(out + (int64_t)t * row_bytes + off) = Row16<E>::pack(acc[u]);
+    }
+  }
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+int elem_bytes(int dtype) {
+  return dtype == PA_F32 ? 4 : (dtype == PA_BF16 || dtype == PA_F16) ? 2 : 0;
+}
+
+int check_tek(int32_t T, int32_t E, int32_t K) {
+  if (T < 0 || E < 1 || K < 1) return PA_EINVAL;
+  if (E > PA_MOE_MAX_EXPERTS || K > PA_MOE_MAX_TOPK || K > E) return PA_EUNSUPPORTED;
+  if ((int64_t)T * K >= ((int64_t)1 << 31) - kSortChunk) return PA_EUNSUPPORTED;
+  return PA_OK;
+}
+
+int check_rows(int32_t T, int32_t K, int32_t hidden, int32_t dtype) {
+  if (T < 0 || K < 1 || hidden < 1) return PA_EINVAL;
+  if (K > PA_MOE_MAX_TOPK) return PA_EUNSUPPORTED;
+  const int eb = elem_bytes(dtype);
+  if (!eb) return PA_EUNSUPPORTED;
+  if (((int64_t)hidden * eb) % 16) return PA_EALIGN;
+  if ((int64_t)T * K >= ((int64_t)1 << 31)) return PA_EUNSUPPORTED;
+  return PA_OK;
+}
+
+hipError_t finish() { return hipGetLastError(); }
+
+}  // namespace
+
+extern "C" {
+
+int pa_moe_topk_softmax(float* topk_weights, int32_t* topk_ids, const float* logits, int32_t T, int32_t E,
+                        int32_t K, int renormalize, void* stream) {
+  const int st = check_tek(T, E, K);
+  if (st != PA_OK) return st;
+  if (T == 0) return PA_OK;
+  if (!topk_weights || !topk_ids || !logits) return PA_EINVAL;
+  if (!aligned(topk_weights, 4) || !aligned(topk_ids, 4) || !aligned(logits, 4)) return PA_EALIGN;
+  (void)hipGetLastError();
+  const dim3 grid((unsigned)((T + 3) / 4)), block(kThreads);
+  hipStream_t s = (hipStream_t)stream;
+  const int vpl = (E + 63) / 64;
+  if (vpl <= 1) hipLaunchKernelGGL(moe_topk_softmax_kernel<1>, grid, block, 0, s, topk_weights, topk_ids, logits, T, E, K, renormalize);
+  else if (vpl <= 2) hipLaunchKernelGGL(moe_topk_softmax_kernel<2>, grid, block, 0, s, topk_weights, topk_ids, logits, T, E, K, renormalize);
+  else if (vpl <= 4) hipLaunchKernelGGL(moe_topk_softmax_kernel<4>, grid, block, 0, s, topk_weights, topk_ids, logits, T, E, K, renormalize);
+  else if (vpl <= 8) hipLaunchKernelGGL(moe_topk_softmax_kernel<8>, grid, block, 0, s, topk_weights, topk_ids, logits, T, E, K, renormalize);
+  else hipLaunchKernelGGL(moe_topk_softmax_kernel<16>, grid, block, 0, s, topk_weights, topk_ids, logits, T, E, K, renormalize);
+  return finish() == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+int64_t pa_moe_sort_workspace_bytes(int32_t T, int32_t E, int32_t K) {
+  const int st = check_tek(T, E, K);
+  if (st != PA_OK) return st;
+  const int64_t N = (int64_t)T * K;
+  const int64_t NC = (N + kSortChunk - 1) / kSortChunk;
+  return (NC * E + N) * (int64_t)sizeof(int32_t);
+}
+
+int pa_moe_sort_by_expert(int32_t* sorted_pairs, int32_t* pair_pos, int32_t* expert_offsets,
+                          const int32_t* topk_ids, int32_t T, int32_t E, int32_t K, void* workspace,
+                          int64_t workspace_bytes, void* stream) {
+  const int st = check_tek(T, E, K);
+  if (st != PA_OK) return st;
+  if (!expert_offsets) return PA_EINVAL;
+  if (!aligned(expert_offsets, 4)) return PA_EALIGN;
+  hipStream_t s = (hipStream_t)stream;
+  const int N = T * K;
+  if (N == 0) {  // every expert's range is empty: the scan alone, over no chunks, writes zero offsets
+    (void)hipGetLastError();
+    hipLaunchKernelGGL(moe_sort_scan_kernel, dim3(1), dim3(PA_MOE_MAX_EXPERTS), 0, s, nullptr, 0, E, 0,
+                       expert_offsets);
+    return finish() == hipSuccess ? PA_OK : PA_EHIP;
+  }
+  if (!sorted_pairs || !pair_pos || !topk_ids || !workspace) return PA_EINVAL;
+  if (!aligned(sorted_pairs, 4) || !aligned(pair_pos, 4) || !aligned(topk_ids, 4) || !aligned(workspace, 4))
+    return PA_EALIGN;
+  if (workspace_bytes < pa_moe_sort_workspace_bytes(T, E, K)) return PA_EINVAL;
+  const int NC = (N + kSortChunk - 1) / kSortChunk;
+  int32_t* counts = reinterpret_cast<int32_t*>(workspace);
+  int32_t* rank = counts + (int64_t)NC * E;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(moe_sort_count_kernel, dim3(NC), dim3(kSortChunk), 0, s, topk_ids, N, E, counts, rank);
+  hipLaunchKernelGGL(moe_sort_scan_kernel, dim3(1), dim3(PA_MOE_MAX_EXPERTS), 0, s, counts, NC, E, N,
+                     expert_offsets);
+  hipLaunchKernelGGL(moe_sort_scatter_kernel, dim3(NC), dim3(kSortChunk), 0, s, topk_ids, N, E, counts, rank,
+                     sorted_pairs, pair_pos);
+  return finish() == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+int pa_moe_permute(void* x_sorted, const void* x, const int32_t* sorted_pairs, int32_t T, int32_t K,
+                   int32_t hidden, int32_t dtype, void* stream) {
+  const int st = check_rows(T, K, hidden, dtype);
+  if (st != PA_OK) return st;
+  if (T == 0) return PA_OK;
+  if (!x_sorted || !x || !sorted_pairs) return PA_EINVAL;
+  if (!aligned(x_sorted, 16) || !aligned(x, 16) || !aligned(sorted_pairs, 4)) return PA_EALIGN;
+  const int N = T * K;
+  const int64_t rb = (int64_t)hidden * elem_bytes(dtype);
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(moe_permute_kernel, dim3((unsigned)((N + 3) / 4)), dim3(kThreads), 0, (hipStream_t)stream,
+                     reinterpret_cast<char*>(x_sorted), reinterpret_cast<const char*>(x), sorted_pairs, N, K, rb);
+  return finish() == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+int pa_moe_combine(void* out, const void* y_sorted, const float* topk_weights, const int32_t* pair_pos,
+                   int32_t T, int32_t K, int32_t hidden, int32_t dtype, void* stream) {
+  const int st = check_rows(T, K, hidden, dtype);
+  if (st != PA_OK) return st;
+  if (T == 0) return PA_OK;
+  if (!out || !y_sorted || !topk_weights || !pair_pos) return PA_EINVAL;
+  if (!aligned(out, 16) || !aligned(y_sorted, 16) || !aligned(topk_weights, 4) || !aligned(pair_pos, 4))
+    return PA_EALIGN;
+  const int64_t rb = (int64_t)hidden * elem_bytes(dtype);
+  const dim3 grid((unsigned)((T + 3) / 4)), block(kThreads);
+  hipStream_t s = (hipStream_t)stream;
+  char* o = reinterpret_cast<char*>(out);
+  const char* y = reinterpret_cast<const char*>(y_sorted);
+  (void)hipGetLastError();
+  if (dtype == PA_F32)
+    hipLaunchKernelGGL(moe_combine_kernel<float>, grid, block, 0, s, o, y, topk_weights, pair_pos, T, K, rb);
+  else if (dtype == PA_BF16)
+    hipLaunchKernelGGL(moe_combine_kernel<__bf16>, grid, block, 0, s, o, y, topk_weights, pair_pos, T, K, rb);
+  else
+    hipLaunchKernelGGL(moe_combine_kernel<_Float16>, grid, block, 0, s, o, y, topk_weights, pair_pos, T, K, rb);
+  return finish() == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+}  // extern "C"

@@ -464,7 +464,7 @@ def moe_bytes(cfg: MoeConfig) -> dict:
     return {
         "topk_softmax": T * E * 4 + N * 8,               # logits in; weights + ids out
         "sort_by_expert": N * 4 + N * 8 + (E + 1) * 4,   # ids in; sorted pairs, positions, offsets out
-        "permute": N * 4 + 2 * N * Hd * e,               # pair list; rows gathered and written
+        "permute": N * 4 + T * Hd * e + N * Hd * e,      # pair list; each token row read once, N rows written
         "combine": N * (4 + 4) + N * Hd * e + T * Hd * e,  # positions, weights; expert rows in; out rows
     }
 

@@ -185,3 +185,33 @@ def test_prefill_validation(lib):
     # empty work: nothing to read, every pointer may be NULL (nothing is launched on the null stream)
     assert lib.pa_prefill(n, n, n, n, n, n, n, ctypes.byref(shape(num_seqs=0)), 0, 0, ctypes.c_float(1.0), n) == L.PA_OK
     assert a is not None
+
+
+def test_moe_validation(lib):
+    n = None
+    a = ctypes.c_void_p(A)
+    f = ctypes.c_float
+    # top-k softmax: sizes, pointers, alignment
+    assert lib.pa_moe_topk_softmax(a, a, a, 10, 2000, 8, 1, n) == L.PA_EUNSUPPORTED      # E > 1024
+    assert lib.pa_moe_topk_softmax(a, a, a, 10, 256, 40, 1, n) == L.PA_EUNSUPPORTED      # K > 32
+    assert lib.pa_moe_topk_softmax(a, a, a, 10, 4, 8, 1, n) == L.PA_EUNSUPPORTED         # K > E
+    assert lib.pa_moe_topk_softmax(a, a, a, -1, 256, 8, 1, n) == L.PA_EINVAL
+    assert lib.pa_moe_topk_softmax(n, a, a, 10, 256, 8, 1, n) == L.PA_EINVAL
+    assert lib.pa_moe_topk_softmax(a, a, ctypes.c_void_p(A + 2), 10, 256, 8, 1, n) == L.PA_EALIGN
+    assert lib.pa_moe_topk_softmax(n, n, n, 0, 256, 8, 1, n) == L.PA_OK                   # T = 0: no-op
+    # sort workspace: (chunks * E + pairs) int32
+    assert lib.pa_moe_sort_workspace_bytes(16384, 256, 8) == (128 * 256 + 131072) * 4
+    assert lib.pa_moe_sort_workspace_bytes(1, 256, 8) == (1 * 256 + 8) * 4
+    assert lib.pa_moe_sort_workspace_bytes(10, 0, 8) == L.PA_EINVAL
+    ws = lib.pa_moe_sort_workspace_bytes(100, 16, 4)
+    assert lib.pa_moe_sort_by_expert(a, a, a, a, 100, 16, 4, a, ws - 4, n) == L.PA_EINVAL   # workspace too small
+    assert lib.pa_moe_sort_by_expert(a, n, a, a, 100, 16, 4, a, ws, n) == L.PA_EINVAL
+    assert lib.pa_moe_sort_by_expert(a, a, a, a, 100, 16, 4, ctypes.c_void_p(A + 1), ws, n) == L.PA_EALIGN
+    # permute / combine: row bytes must be a multiple of 16, dtype known
+    assert lib.pa_moe_permute(a, a, a, 10, 8, 2047, L.PA_BF16, n) == L.PA_EALIGN
+    assert lib.pa_moe_permute(a, a, a, 10, 8, 2048, 9, n) == L.PA_EUNSUPPORTED
+    assert lib.pa_moe_permute(a, ctypes.c_void_p(A + 8), a, 10, 8, 2048, L.PA_BF16, n) == L.PA_EALIGN
+    assert lib.pa_moe_combine(a, a, a, n, 10, 8, 2048, L.PA_BF16, n) == L.PA_EINVAL
+    assert lib.pa_moe_combine(a, a, a, a, 10, 40, 2048, L.PA_BF16, n) == L.PA_EUNSUPPORTED
+    assert lib.pa_moe_combine(n, n, n, n, 0, 8, 2048, L.PA_F32, n) == L.PA_OK
+    assert f is not None

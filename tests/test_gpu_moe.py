@@ -1,0 +1,183 @@
+"""GPU parity of the MoE routing path (through the C ABI) against the oracle
+(oracle.moe).
+
+Integer results (expert ids, sorted pairs, positions, offsets, permuted rows)
+must match exactly. Weights: max |error| <= 2e-6 (fp32 softmax with the
+hardware exp against fp64). Combine: max |error| <= 2e-2 for bf16 outputs
+(rounding of values up to ~4), 1e-5 for fp32.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.moe as om
+import paged_attention_decode_06_amd as pa
+from paged_attention_decode_06_amd import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("needs a GPU")
+    pa.load()
+    return torch.device("cuda:0")
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def to_dev(a, dev):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def topk(logits, K, renorm, dev):
+    T = logits.shape[0]
+    lg = torch.from_numpy(logits).to(dev)
+    w = torch.full((T, K), float("nan"), dtype=torch.float32, device=dev)
+    i = torch.full((T, K), -1, dtype=torch.int32, device=dev)
+    pa.pa_moe_topk_softmax(w, i, lg, renorm)
+    torch.cuda.synchronize(dev)
+    return w.cpu().numpy(), i.cpu().numpy()
+
+
+def sort(ids, E, dev):
+    T, K = ids.shape
+    t_ids = torch.from_numpy(np.ascontiguousarray(ids, dtype=np.int32)).to(dev)
+    sp = torch.full((T * K,), -1, dtype=torch.int32, device=dev)
+    pp = torch.full((T * K,), -1, dtype=torch.int32, device=dev)
+    off = torch.full((E + 1,), -1, dtype=torch.int32, device=dev)
+    ws = torch.full((max(pa.moe_sort_workspace_bytes(T, E, K) // 4, 1),), 12345, dtype=torch.int32, device=dev)
+    pa.pa_moe_sort_by_expert(sp, pp, off, t_ids, E, ws)
+    torch.cuda.synchronize(dev)
+    return sp.cpu().numpy(), pp.cpu().numpy(), off.cpu().numpy()
+
+
+@pytest.mark.parametrize("T,E,K", [(1000, 256, 8), (37, 64, 1), (300, 100, 8), (64, 1024, 32), (5, 8, 8),
+                                   (129, 256, 2)])
+@pytest.mark.parametrize("renorm", [False, True])
+def test_topk_softmax(dev, T, E, K, renorm):
+    rng = np.random.default_rng(T + E + K)
+    lg = rng.standard_normal((T, E)).astype(np.float32)
+    say(f"topk softmax T={T} E={E} K={K} renorm={renorm}")
+    w, i = topk(lg, K, renorm, dev)
+    ow, oi = om.topk_softmax(lg, K, renorm)
+    assert np.array_equal(i, oi)
+    assert np.abs(w - ow).max() <= 2e-6
+
+
+def test_topk_ties_go_to_the_lower_id(dev):
+    rng = np.random.default_rng(1)
+    lg = (np.round(rng.standard_normal((500, 256)) * 2) / 2).astype(np.float32)   # many exact ties
+    lg[0, :] = 1.5                                                                   # all tied
+    say("topk with ties")
+    w, i = topk(lg, 8, True, dev)
+    ow, oi = om.topk_softmax(lg, 8, True)
+    assert np.array_equal(i, oi)
+    assert i[0].tolist() == list(range(8))
+    assert np.abs(w - ow).max() <= 2e-6
+
+
+@pytest.mark.parametrize("T,E,K,dist", [(16384, 256, 8, "uniform"), (1, 256, 8, "uniform"), (100, 7, 3, "uniform"),
+                                        (2000, 1024, 4, "uniform"), (3000, 256, 8, "one"), (777, 256, 8, "skew"),
+                                        (129, 16, 8, "uniform")])
+def test_sort_by_expert_exact(dev, T, E, K, dist):
+    rng = np.random.default_rng(T * 7 + E)
+    if dist == "uniform":
+        ids = rng.integers(0, E, size=(T, K))
+    elif dist == "one":
+        ids = np.full((T, K), E // 2)
+    else:
+        ids = np.minimum(rng.geometric(0.3, size=(T, K)) - 1, E - 1)
+    ids = ids.astype(np.int32)
+    say(f"sort by expert T={T} E={E} K={K} ({dist})")
+    sp, pp, off = sort(ids, E, dev)
+    osp, opp, ooff = om.sort_by_expert(ids, E)
+    assert np.array_equal(off, ooff)
+    assert np.array_equal(sp, osp)
+    assert np.array_equal(pp, opp)
+
+
+def test_sort_out_of_range_ids_stay_in_bounds(dev):
+    ids = np.array([[0, 5], [-3, 99], [2, 1]], dtype=np.int32)   # -3 and 99 are data errors for E = 6
+    say("sort with out-of-range ids (clamped)")
+    sp, pp, off = sort(ids, 6, dev)
+    clamped = np.clip(ids, 0, 5)
+    osp, opp, ooff = om.sort_by_expert(clamped, 6)
+    assert np.array_equal(sp, osp) and np.array_equal(pp, opp) and np.array_equal(off, ooff)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
+def test_permute_is_an_exact_gather(dev, dtype):
+    cfg = W.MoeConfig("perm", 300, 64, 4, 256, dtype)
+    x = W.make_moe_inputs(cfg, seed=5)
+    rng = np.random.default_rng(5)
+    ids = rng.integers(0, 64, size=(300, 4)).astype(np.int32)
+    osp, _, _ = om.sort_by_expert(ids, 64)
+    xs = torch.empty((1200, 256), dtype=to_dev(x.x[:1], dev).dtype, device=dev)
+    say(f"permute {dtype}")
+    pa.pa_moe_permute(xs, to_dev(x.x, dev), torch.from_numpy(osp).to(dev), 4)
+    torch.cuda.synchronize(dev)
+    got = xs.cpu().view(torch.int16).numpy() if dtype == "bf16" else xs.cpu().numpy()
+    want = om.permute_rows(x.x, osp, 4)
+    assert np.array_equal(got.view(want.dtype), want)
+
+
+@pytest.mark.parametrize("dtype,tol", [("bf16", 2e-2), ("f32", 1e-5), ("f16", 1e-2)])
+def test_combine(dev, dtype, tol):
+    cfg = W.MoeConfig("comb", 500, 128, 8, 512, dtype)
+    x = W.make_moe_inputs(cfg, seed=6)
+    ow, oi = om.topk_softmax(x.logits, 8, True)
+    _, opp, _ = om.sort_by_expert(oi, 128)
+    out = torch.full((500, 512), float("nan"), dtype=to_dev(x.x[:1], dev).dtype, device=dev)
+    say(f"combine {dtype}")
+    pa.pa_moe_combine(out, to_dev(x.y_sorted, dev), torch.from_numpy(ow.astype(np.float32)).to(dev),
+                      torch.from_numpy(opp).to(dev))
+    torch.cuda.synchronize(dev)
+    got = W.from_device(out)
+    want = om.combine(W.bf16_bits_to_f32(x.y_sorted).astype(np.float64) if dtype == "bf16"
+                      else x.y_sorted.astype(np.float64), ow.astype(np.float32), opp)
+    assert np.abs(got - want).max() <= tol
+
+
+@pytest.mark.parametrize("num", [1, 2])
+def test_moe_routing_workload_end_to_end(dev, num):
+    """topk -> sort -> permute -> (expert GEMMs: stand-in outputs) -> combine at full size."""
+    x = W.make_moe_inputs(num)
+    c = x.cfg
+    T, E, K, Hd = c.num_tokens, c.num_experts, c.top_k, c.hidden
+    say(f"MoE routing workload {num} {c.name}")
+    w, i = topk(x.logits, K, c.renormalize, dev)
+    ow, oi = om.topk_softmax(x.logits, K, c.renormalize)
+    assert np.array_equal(i, oi)
+    assert np.abs(w - ow).max() <= 2e-6
+    sp, pp, off = sort(i, E, dev)
+    osp, opp, ooff = om.sort_by_expert(oi, E)
+    assert np.array_equal(sp, osp) and np.array_equal(pp, opp) and np.array_equal(off, ooff)
+    xs = torch.empty((T * K, Hd), dtype=torch.bfloat16, device=dev)
+    pa.pa_moe_permute(xs, to_dev(x.x, dev), torch.from_numpy(sp).to(dev), K)
+    out = torch.empty((T, Hd), dtype=torch.bfloat16, device=dev)
+    pa.pa_moe_combine(out, to_dev(x.y_sorted, dev), torch.from_numpy(w).to(dev), torch.from_numpy(pp).to(dev))
+    torch.cuda.synchronize(dev)
+    rows = np.random.default_rng(num).choice(T * K, size=min(4096, T * K), replace=False)
+    got = xs.cpu().view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got[rows], x.x[osp[rows] // K])
+    want = om.combine(W.bf16_bits_to_f32(x.y_sorted).astype(np.float64), w, pp)
+    assert np.abs(W.from_device(out) - want).max() <= 2e-2
+
+
+def test_moe_empty(dev):
+    say("MoE with no tokens")
+    e = torch.empty((0, 8), dtype=torch.float32, device=dev)
+    pa.pa_moe_topk_softmax(e, torch.empty((0, 8), dtype=torch.int32, device=dev),
+                           torch.empty((0, 256), dtype=torch.float32, device=dev))
+    off = torch.full((257,), -1, dtype=torch.int32, device=dev)
+    z = torch.empty((0,), dtype=torch.int32, device=dev)
+    pa.pa_moe_sort_by_expert(z, z, off, torch.empty((0, 8), dtype=torch.int32, device=dev), 256,
+                             torch.empty((1,), dtype=torch.int32, device=dev))
+    torch.cuda.synchronize(dev)
+    assert (off.cpu().numpy() == 0).all()

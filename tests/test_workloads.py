@@ -142,6 +142,6 @@ def test_moe_inputs_shapes_and_bytes():
     y = W.make_moe_inputs(2)
     assert np.array_equal(x.logits, y.logits) and np.array_equal(x.y_sorted, y.y_sorted)
     b = W.moe_bytes(c)
-    assert b["permute"] == 256 * 8 * 4 + 2 * 256 * 8 * 2048 * 2
+    assert b["permute"] == 256 * 8 * 4 + 256 * 2048 * 2 + 256 * 8 * 2048 * 2
     small = W.make_moe_inputs(1, num_tokens=10)
     assert small.x.shape == (10, 2048)
