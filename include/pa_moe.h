@@ -64,7 +64,8 @@ int64_t pa_moe_sort_workspace_bytes(int32_t T, int32_t E, int32_t K);
  *   topk_ids        int32 [T, K]  values in [0, E)
  *   workspace       >= pa_moe_sort_workspace_bytes(T, E, K) bytes, 4-byte
  *                   aligned; its contents on entry do not matter.
- * Three launches (per-chunk counts and ranks, a scan, the scatter). */
+ * Four launches (per-chunk ranks and counts, a scan over chunks per expert,
+ * the expert offsets, the scatter). */
 int pa_moe_sort_by_expert(int32_t* sorted_pairs, int32_t* pair_pos, int32_t* expert_offsets,
                           const int32_t* topk_ids, int32_t T, int32_t E, int32_t K, void* workspace,
                           int64_t workspace_bytes, void* stream);

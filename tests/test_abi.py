@@ -199,9 +199,9 @@ def test_moe_validation(lib):
     assert lib.pa_moe_topk_softmax(n, a, a, 10, 256, 8, 1, n) == L.PA_EINVAL
     assert lib.pa_moe_topk_softmax(a, a, ctypes.c_void_p(A + 2), 10, 256, 8, 1, n) == L.PA_EALIGN
     assert lib.pa_moe_topk_softmax(n, n, n, 0, 256, 8, 1, n) == L.PA_OK                   # T = 0: no-op
-    # sort workspace: (chunks * E + pairs) int32
-    assert lib.pa_moe_sort_workspace_bytes(16384, 256, 8) == (128 * 256 + 131072) * 4
-    assert lib.pa_moe_sort_workspace_bytes(1, 256, 8) == (1 * 256 + 8) * 4
+    # sort workspace: (chunks * E + pairs + E) int32
+    assert lib.pa_moe_sort_workspace_bytes(16384, 256, 8) == (128 * 256 + 131072 + 256) * 4
+    assert lib.pa_moe_sort_workspace_bytes(1, 256, 8) == (1 * 256 + 8 + 256) * 4
     assert lib.pa_moe_sort_workspace_bytes(10, 0, 8) == L.PA_EINVAL
     ws = lib.pa_moe_sort_workspace_bytes(100, 16, 4)
     assert lib.pa_moe_sort_by_expert(a, a, a, a, 100, 16, 4, a, ws - 4, n) == L.PA_EINVAL   # workspace too small
