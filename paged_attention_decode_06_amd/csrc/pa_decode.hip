@@ -1306,7 +1306,6 @@ hipError_t nothing_launched(const Launch& L) {
 
 template <typename T, int D, int NW, int TB>
 hipError_t launch_h16(const Params& P, bool trace, dim3 grid, const Launch& L) {
-  constexpr int NACC = (D / 128) * 8;
   constexpr bool QLDS = (D == 128) ? PA_D128_Q_LDS : PA_D256_Q_LDS;
   const size_t head = (size_t)2 * NW * 16 * sizeof(float);
   const size_t qarea = QLDS ? (size_t)(D / 32) * 64 * 16 : 0;

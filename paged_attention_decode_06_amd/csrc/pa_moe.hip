@@ -10,8 +10,8 @@
 //
 // Design (wave64):
 //   * top-k softmax: one wave per token, E/64 logits per lane; max and sum by
-//     xor trees, then K rounds of a wave-wide argmax on (logit, -id) with a
-//     per-lane bitmask of experts already taken.
+//     DPP reductions, then K rounds of (wave max of the untaken logits, the
+//     lowest id holding it by ballots).
 //   * sort: a stable counting sort in four launches. Chunks of 1024 pairs:
 //     every pair's rank among the earlier same-expert pairs of its chunk
 //     (wave ballots, then a prefix over the chunk's waves) and the chunk's
@@ -54,6 +54,37 @@ __device__ __forceinline__ void st_rows(void* p, u32x4 v) {
 }
 
 // ---------------------------------------------------------------- top-k softmax
+// Wave-wide reductions on DPP lane moves (no LDS crossbar): swaps within
+// quads, mirrors within half rows and rows, then the row broadcasts that
+// fold rows 0-2 into row 3; lane 63 ends with the result, read back as a
+// uniform value. The combining order is fixed, so sums are reproducible.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_move(float v) {  // lanes outside ROWS keep v
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                                               CTRL, ROWS, 0xf, false));
+}
+
+template <typename Op>
+__device__ __forceinline__ float wave_reduce(float x, Op op) {
+  x = op(x, dpp_move<0xb1, 0xf>(x));   // quad_perm [1,0,3,2]
+  x = op(x, dpp_move<0x4e, 0xf>(x));   // quad_perm [2,3,0,1]
+  x = op(x, dpp_move<0x141, 0xf>(x));  // row_half_mirror
+  x = op(x, dpp_move<0x140, 0xf>(x));  // row_mirror: every lane holds its row's result
+  x = op(x, dpp_move<0x142, 0xa>(x));  // row_bcast:15 into rows 1 and 3
+  x = op(x, dpp_move<0x143, 0xc>(x));  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), 63));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  return wave_reduce(x, [](float a, float b) { return fmaxf(a, b); });
+}
+__device__ __forceinline__ float wave_sum(float x) {
+  return wave_reduce(x, [](float a, float b) { return a + b; });
+}
+
+// One wave per token. Round j: the wave maximum of the logits not yet taken
+// (DPP reduction), then the lowest expert id holding it: for u = 0, 1, ...
+// the ballot of lanes whose u-th logit is that maximum and untaken; the first
+// non-empty ballot's lowest lane wins (id = lane + 64u).
 template <int VPL>
 __global__ __launch_bounds__(kThreads) void moe_topk_softmax_kernel(float* __restrict__ w_out,
                                                                     int32_t* __restrict__ id_out,
@@ -72,53 +103,44 @@ __global__ __launch_bounds__(kThreads) void moe_topk_softmax_kernel(float* __res
   float m = v[0];
 #pragma unroll
   for (int u = 1; u < VPL; ++u) m = fmaxf(m, v[u]);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
-  float sum = 0.f;
+  m = wave_max(m);
+  float part = 0.f;
 #pragma unroll
   for (int u = 0; u < VPL; ++u)
-    if (lane + 64 * u < E) sum += __builtin_amdgcn_exp2f((v[u] - m) * kLog2e);
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    if (lane + 64 * u < E) part += __builtin_amdgcn_exp2f((v[u] - m) * kLog2e);
+  const float sum = wave_sum(part);
 
-  uint32_t taken = 0;  // bit u: expert lane + 64u already chosen
+  bool avail[VPL];
+#pragma unroll
+  for (int u = 0; u < VPL; ++u) avail[u] = lane + 64 * u < E && !(v[u] != v[u]);  // NaN never chosen
   float my_w = 0.f;
   int my_id = 0;
   for (int j = 0; j < K; ++j) {
-    float bv = -INFINITY;
-    int bi = 0x7fffffff;
+    float lm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < VPL; ++u)
+      if (avail[u]) lm = fmaxf(lm, v[u]);
+    const float best = wave_max(lm);
+    int id = -1;
 #pragma unroll
     for (int u = 0; u < VPL; ++u) {
-      const int e = lane + 64 * u;
-      if (e < E && !((taken >> u) & 1u) && (v[u] > bv || (v[u] == bv && e < bi))) {
-        bv = v[u];
-        bi = e;
+      if (id < 0) {
+        const uint64_t hit = __builtin_amdgcn_ballot_w64(avail[u] && v[u] == best);
+        if (hit) {
+          const int l = __builtin_ctzll(hit);
+          id = l + 64 * u;
+          if (lane == l) avail[u] = false;
+        }
       }
     }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float ov = __shfl_xor(bv, o);
-      const int oi = __shfl_xor(bi, o);
-      if (ov > bv || (ov == bv && oi < bi)) {
-        bv = ov;
-        bi = oi;
-      }
-    }
-    if (bi >= E) {  // only NaN logits left: a data error, kept in range
-      bi = 0;
-      bv = -INFINITY;
-    } else if ((bi & 63) == lane) {
-      taken |= 1u << (bi >> 6);
-    }
+    if (id < 0) id = 0;  // nothing left but NaN logits: a data error, kept in range
     if (lane == j) {
-      my_w = (bv > -INFINITY) ? __builtin_amdgcn_exp2f((bv - m) * kLog2e) / sum : 0.f;
-      my_id = bi;
+      my_w = (id >= 0 && best > -INFINITY) ? __builtin_amdgcn_exp2f((best - m) * kLog2e) / sum : 0.f;
+      my_id = id;
     }
   }
   if (renorm) {
-    float s = lane < K ? my_w : 0.f;
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) s += __shfl_xor(s, o);
+    const float s = wave_sum(lane < K ? my_w : 0.f);
     if (s > 0.f) my_w /= s;
   }
   if (lane < K) {
