@@ -47,7 +47,9 @@ if ROOT not in sys.path:
 METRIC = "paged-attn decode achieved HBM GB/s (% of peak) + µs/step at 100K ctx"
 PEAK_GBS = 8000.0
 SCRUB_BYTES = 1 << 30
-KERNEL_SRC = os.path.join(ROOT, "paged_attention_decode_06_amd", "csrc", "pa_decode.hip")
+CSRC = os.path.join(ROOT, "paged_attention_decode_06_amd", "csrc")
+# Sources of the decode kernels (the counter summary is tied to these bytes)
+KERNEL_SRCS = [os.path.join(CSRC, "pa_decode.hip"), os.path.join(CSRC, "pa_common.h")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_counters.txt")
 
 
@@ -55,9 +57,11 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-
-def kernel_source_hash() -> str:
-    return hashlib.sha256(open(KERNEL_SRC, "rb").read()).hexdigest()[:16]
+def kernel_source_hash(paths=None) -> str:
+    h = hashlib.sha256()
+    for p in (paths or KERNEL_SRCS):
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def workload_label(x, ps: int = 512) -> dict:
@@ -393,7 +397,8 @@ def bench_prefill(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: fl
         "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tf / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "pa_prefill",
                      "flops_per_launch": int(flops)},
-        "kernel_source_sha256_16": kernel_source_hash(),
+        "kernel_source_sha256_16": kernel_source_hash([os.path.join(CSRC, "pa_prefill.hip"),
+                                                       os.path.join(CSRC, "pa_common.h")]),
     }
     res["cpu_baseline"] = prefill_cpu_baseline(x, out, cpu_budget) if cpu_budget > 0 else None
     del scrub_buf

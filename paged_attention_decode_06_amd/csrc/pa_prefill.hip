@@ -1,0 +1,399 @@
+// Prefix / chunked-prefill attention over the paged cache for gfx950 (MI355X):
+// the kernel and its C ABI entry point (pa_prefill, declared in pa_decode.h).
+
+#include <algorithm>
+
+#include "pa_common.h"
+
+namespace {
+
+// ---------------------------------------------------------------- prefix / chunked prefill
+// Attention of a chunk of query tokens over the paged cache (project_6 commit
+// cd0d9e1a, "paged_attn.py rewrite" item 1 and the Triton prefill note: the
+// context's K/V come from the cache, query tiles walk key tiles with the
+// online softmax; project_6 blame of optimizations/prefix_prefill_patch.py:
+// query tiles against key/value tiles, head_dim 128/256, GQA, fp16/bf16).
+// Sequence s keeps L tokens in the cache, the last Q of them the chunk; chunk
+// token i sits at position L - Q + i and sees cached tokens 0 .. L - Q + i.
+//
+// The decode tile layout carries over with query rows on the MFMA N axis: a
+// row is one (chunk token, query head of the GQA group), row = token * G +
+// head, so one K/V tile serves every head of the group and QT tokens. One
+// workgroup takes (sequence, KV head, QT-token query tile); each of its NW
+// waves owns NTW N-tiles of 16 rows and walks every key tile itself (no merge
+// across waves). K/V tiles are read with cacheable loads: the workgroup's
+// waves read the same tiles at about the same time and share them through
+// the L1/L2. K goes through the wave-private swizzled LDS tile; V is
+// transposed in registers; P is the QK accumulator rounded to the 16-bit
+// type. Outputs are stored straight from the accumulators (8 consecutive dims
+// per 16-byte store).
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* bt;
+  const int32_t* sl;
+  const int32_t* qsl;
+  void* out;
+  int64_t NB;
+  int S, H, Hkv, G, MB, T, QT;
+  float scale2;
+};
+
+template <typename T, int D, int NW, int NTW, int TB, bool PF>
+__global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
+  typedef typename H16<T>::x8 tx8;
+  typedef typename H16<T>::x4 tx4;
+  extern __shared__ float smem[];
+  constexpr int KK = D / 32;    // QK MFMAs per block and N-tile
+  constexpr int NH = D / 128;
+  constexpr int NACC = NH * 8;  // output tiles per N-tile
+  constexpr int CH = 64 / TB;   // tiles per block-id refill
+  constexpr int KCH = D / 8;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int g = lane & 15, grp = lane >> 4;
+
+  const int pairs = P.S * P.Hkv;
+  const int pair = blockIdx.x % pairs, qt = blockIdx.x / pairs;
+  const int s = pair / P.Hkv, kvh = pair % P.Hkv;
+  // Extents, clamped so that no data value can send a read out of bounds.
+  int qb = P.qsl[s], qe = P.qsl[s + 1];
+  qb = min(max(qb, 0), P.T);
+  qe = min(max(qe, qb), P.T);
+  const int Q = qe - qb;
+  int L = P.sl[s];
+  L = min(max(L, 0), P.MB * kBS);
+  const int i0 = qt * P.QT;
+  if (i0 >= Q) return;
+  const int i1 = min(i0 + P.QT, Q);
+  const int base = L - Q;                   // position of chunk token 0 (negative: no keys)
+  const int kmax = min(L, base + i1);       // the tile's rows see keys [0, kmax)
+
+  // This lane's row in each of the wave's N-tiles.
+  int tokr[NTW], posc[NTW];
+  bool valid[NTW], live[NTW];
+#pragma unroll
+  for (int jj = 0; jj < NTW; ++jj) {
+    const int row = (w * NTW + jj) * 16 + g;
+    const int tok = i0 + row / P.G;
+    valid[jj] = row < P.QT * P.G && tok < i1;
+    tokr[jj] = tok;
+    const int pos = base + tok;
+    live[jj] = valid[jj] && pos >= 0;
+    posc[jj] = live[jj] ? pos : kmax - 1;   // rows without keys compute a harmless stand-in
+  }
+  auto out_row = [&](int jj) -> T* {
+    const int row = (w * NTW + jj) * 16 + g;
+    return reinterpret_cast<T*>(P.out) + ((int64_t)(qb + tokr[jj]) * P.H + kvh * P.G + row % P.G) * D;
+  };
+
+  if (kmax <= 0) {  // no row of the tile sees a key
+#pragma unroll
+    for (int jj = 0; jj < NTW; ++jj)
+      if (valid[jj] && grp == 0)
+        for (int d = 0; d < D; d += 4) store4<T>(out_row(jj), d, (f32x4){0.f, 0.f, 0.f, 0.f});
+    return;
+  }
+
+  // B operands of the QK MFMA: lane holds q[row][kk*32 + 8*grp .. +8].
+  tx8 qv[NTW][KK];
+#pragma unroll
+  for (int jj = 0; jj < NTW; ++jj) {
+    const int row = (w * NTW + jj) * 16 + g;
+    const T* qrow = reinterpret_cast<const T*>(P.q) +
+                    ((int64_t)(qb + tokr[jj]) * P.H + kvh * P.G + row % P.G) * D;
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (valid[jj]) x = ld16(qrow + kk * 32 + grp * 8);
+      qv[jj][kk] = __builtin_bit_cast(tx8, x);
+    }
+  }
+
+  u32x4* ktile = reinterpret_cast<u32x4*>(smem) + (size_t)w * TB * 16 * KCH;
+  const int64_t head_elems = (int64_t)kBS * D;
+  const int64_t block_elems = head_elems * P.Hkv;
+  const T* kbase = reinterpret_cast<const T*>(P.k) + kvh * head_elems;
+  const T* vbase = reinterpret_cast<const T*>(P.v) + kvh * head_elems;
+  const int32_t* bt_row = P.bt + (int64_t)s * P.MB;
+  const int nblk = (kmax + kBS - 1) / kBS;
+  const int ntiles = (nblk + TB - 1) / TB;
+
+  float m[NTW], lsum[NTW];
+  f32x4 acc[NTW][NACC];
+#pragma unroll
+  for (int jj = 0; jj < NTW; ++jj) {
+    m[jj] = -INFINITY;
+    lsum[jj] = 0.f;
+#pragma unroll
+    for (int a = 0; a < NACC; ++a) acc[jj][a] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  }
+
+  // Physical ids of the next CH tiles: lane j holds block (k * CH * TB + j).
+  int ids = 0;
+  auto refill = [&](int k) {
+    const int blk = k * CH * TB + lane;
+    int id = -1;
+    if (lane < CH * TB && blk < nblk) {
+      id = bt_row[blk];
+      if ((uint64_t)(int64_t)id >= (uint64_t)P.NB) id = 0;  // out-of-range ids read block 0
+    }
+    ids = id;
+  };
+
+  // Issues tile t's loads (tiles are issued in order, so the id list is
+  // refilled exactly when a new CH-tile chunk starts).
+  auto issue = [&](BTile<D, TB>& tl, int t) {
+    if (t % CH == 0) refill(t / CH);
+    int64_t phys[TB];
+    bool vb[TB];
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      vb[b] = t * TB + b < nblk;
+      phys[b] = __builtin_amdgcn_readlane(ids, (t % CH) * TB + b);
+    }
+    issue_tile<T, D, TB, false>(tl, kbase, vbase, block_elems, phys, vb, g, grp);
+  };
+
+  auto compute = [&](BTile<D, TB>& tl, int t) {
+
+    // K: registers -> swizzled LDS tile -> MFMA A operands.
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const int row = 4 * grp + rr, c16 = 16 * h + g;
+          ktile[(b * 16 + row) * KCH + (c16 ^ row)] = tl.k[b][rr][h];
+        }
+    tx8 ka[TB][KK];
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int c16 = 4 * kk + grp;
+        ka[b][kk] = __builtin_bit_cast(tx8, ktile[(b * 16 + g) * KCH + (c16 ^ g)]);
+      }
+
+    const int tok0 = t * TB * kBS;
+    // V rows at or past kmax (tail slots of the last block, blocks past the
+    // end) are zeroed: a zero weight times NaN would poison the sum.
+    if (tok0 + TB * kBS > kmax) {
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+          if (tok0 + b * kBS + 4 * grp + rr >= kmax)
+#pragma unroll
+            for (int h = 0; h < NH; ++h) tl.v[b][rr][h] = (u32x4){0u, 0u, 0u, 0u};
+    }
+
+#pragma unroll
+    for (int jj = 0; jj < NTW; ++jj) {
+      f32x4 sc[TB];
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        sc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) sc[b] = H16<T>::mma32(ka[b][kk], qv[jj][kk], sc[b]);
+      }
+      float x[TB][4];
+      float mx = -INFINITY;
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int kp = tok0 + b * kBS + 4 * grp + i;
+          const float z = (kp <= posc[jj]) ? sc[b][i] * P.scale2 : -INFINITY;
+          x[b][i] = z;
+          mx = fmaxf(mx, z);
+        }
+      mx = group_max(mx);
+      const float mnew = fmaxf(m[jj], mx);  // finite: key 0 is in every row's first tile
+      const float alpha = fast_exp2(m[jj] - mnew);
+      m[jj] = mnew;
+      T pb[TB][4];
+      float ps = 0.f;
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pb[b][i] = (T)fast_exp2(x[b][i] - mnew);
+          ps += (float)pb[b][i];
+        }
+      lsum[jj] = lsum[jj] * alpha + ps;
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) acc[jj][a] *= alpha;
+      }
+      if constexpr (TB == 2) {
+        tx8 pv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = pb[0][i];
+          pv[4 + i] = pb[1][i];
+        }
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int c = j >> 1;
+            u32x4 a;
+            if (j & 1) {
+              a[0] = pack_hi(tl.v[0][0][h][c], tl.v[0][1][h][c]);
+              a[1] = pack_hi(tl.v[0][2][h][c], tl.v[0][3][h][c]);
+              a[2] = pack_hi(tl.v[1][0][h][c], tl.v[1][1][h][c]);
+              a[3] = pack_hi(tl.v[1][2][h][c], tl.v[1][3][h][c]);
+            } else {
+              a[0] = pack_lo(tl.v[0][0][h][c], tl.v[0][1][h][c]);
+              a[1] = pack_lo(tl.v[0][2][h][c], tl.v[0][3][h][c]);
+              a[2] = pack_lo(tl.v[1][0][h][c], tl.v[1][1][h][c]);
+              a[3] = pack_lo(tl.v[1][2][h][c], tl.v[1][3][h][c]);
+            }
+            acc[jj][h * 8 + j] = H16<T>::mma32(__builtin_bit_cast(tx8, a), pv, acc[jj][h * 8 + j]);
+          }
+      } else {
+        tx4 pv4;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pv4[i] = pb[0][i];
+#pragma unroll
+        for (int h = 0; h < NH; ++h)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int c = j >> 1;
+            u32x2 a;
+            if (j & 1) {
+              a[0] = pack_hi(tl.v[0][0][h][c], tl.v[0][1][h][c]);
+              a[1] = pack_hi(tl.v[0][2][h][c], tl.v[0][3][h][c]);
+            } else {
+              a[0] = pack_lo(tl.v[0][0][h][c], tl.v[0][1][h][c]);
+              a[1] = pack_lo(tl.v[0][2][h][c], tl.v[0][3][h][c]);
+            }
+            acc[jj][h * 8 + j] = H16<T>::mma16(__builtin_bit_cast(tx4, a), pv4, acc[jj][h * 8 + j]);
+          }
+      }
+    }
+  };
+
+  BTile<D, TB> A;
+  issue(A, 0);
+  if constexpr (PF) {
+    // Two register stages: the next tile's loads are in flight while this
+    // tile's math runs (a workgroup's waves are few per SIMD here).
+    BTile<D, TB> B;
+    for (int t = 0;;) {
+      if (t + 1 < ntiles) issue(B, t + 1);
+      compute(A, t);
+      if (t + 1 >= ntiles) break;
+      if (t + 2 < ntiles) issue(A, t + 2);
+      compute(B, t + 1);
+      if (t + 2 >= ntiles) break;
+      t += 2;
+    }
+  } else {
+    for (int t = 0;;) {
+      compute(A, t);
+      if (++t >= ntiles) break;
+      issue(A, t);
+    }
+  }
+
+  // acc[jj][h*8 + j][i] holds dim 128h + 32*grp + 8i + j of the lane's row:
+  // for fixed (h, i) the 8 values j = 0..7 are consecutive dims.
+#pragma unroll
+  for (int jj = 0; jj < NTW; ++jj) {
+    const float tot = group_sum(lsum[jj]);
+    if (!valid[jj]) continue;
+    const float inv = live[jj] ? 1.f / tot : 0.f;
+    T* orow = out_row(jj);
+#pragma unroll
+    for (int h = 0; h < NH; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        typename H16<T>::x8 o;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) o[j] = (T)(acc[jj][h * 8 + j][i] * inv);
+        *reinterpret_cast<typename H16<T>::x8*>(orow + 128 * h + 32 * grp + 8 * i) = o;
+      }
+  }
+}
+
+// Prefill launch shape: 128 query rows per workgroup (QT tokens x G heads).
+// D=128, at most kPrefillSmallGrid workgroups (one or two per CU, long
+// contexts): 8 waves x 1 N-tile, two-block tiles, next tile prefetched into
+// registers, since few waves share a SIMD; larger grids: 4 waves x 2 N-tiles,
+// one-block tiles, no prefetch (2 waves per SIMD resident). D=256: 8 waves x 1
+// N-tile, one-block tiles (register budget). Measured on the four prefill
+// workloads against the other combinations of these knobs.
+constexpr int kPrefillRows = 128;
+constexpr int kPrefillMaxNW = 8;  // waves per workgroup, largest launch shape
+constexpr int64_t kPrefillSmallGrid = 512;
+
+template <typename T>
+hipError_t launch_prefill_t(const PrefillParams& P, int D, int nqt, const Launch& L) {
+  const dim3 grid((unsigned)((int64_t)P.S * P.Hkv * nqt));
+  if (grid.x == 0) return nothing_launched(L);
+  if (D == 128) {
+    if ((int64_t)grid.x <= kPrefillSmallGrid) {
+      constexpr int NW = 8, NTW = 1, TB = 2;
+      const size_t smem = (size_t)NW * TB * 16 * 128 * sizeof(T);
+      return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true>, grid, dim3(NW * 64), smem, L, P);
+    }
+    constexpr int NW = 4, NTW = 2, TB = 1;
+    const size_t smem = (size_t)NW * TB * 16 * 128 * sizeof(T);
+    return launch(pa_prefill_h16<T, 128, NW, NTW, TB, false>, grid, dim3(NW * 64), smem, L, P);
+  }
+  constexpr int NW = 8, NTW = 1, TB = 1;
+  const size_t smem = (size_t)NW * TB * 16 * 256 * sizeof(T);
+  return launch(pa_prefill_h16<T, 256, NW, NTW, TB, false>, grid, dim3(NW * 64), smem, L, P);
+}
+
+int check_prefill(const void* out, const void* q, const void* k, const void* v, const int32_t* bt,
+                  const int32_t* sl, const int32_t* qsl, const pa_shape* sh, int32_t T, int32_t maxq) {
+  const int st = check_shape(sh);
+  if (st != PA_OK) return st;
+  if (sh->dtype != PA_BF16 && sh->dtype != PA_F16) return PA_EUNSUPPORTED;
+  if (T < 0 || maxq < 0) return PA_EINVAL;
+  if (sh->num_seqs == 0 || T == 0 || maxq == 0) return PA_OK;  // nothing is read or written
+  if (!out || !q || !k || !v || !bt || !sl || !qsl) return PA_EINVAL;
+  if (!aligned(out, 16) || !aligned(q, 16) || !aligned(k, 16) || !aligned(v, 16) || !aligned(bt, 4) ||
+      !aligned(sl, 4) || !aligned(qsl, 4))
+    return PA_EALIGN;
+  const int G = sh->num_heads / sh->num_kv_heads;
+  const int64_t qt = kPrefillRows / G;
+  const int64_t wgs = (int64_t)sh->num_seqs * sh->num_kv_heads * ((maxq + qt - 1) / qt);
+  if (wgs >= ((int64_t)1 << 31) / (kPrefillMaxNW * 64)) return PA_EUNSUPPORTED;
+  if ((int64_t)T * sh->num_heads * sh->head_dim >= ((int64_t)1 << 62)) return PA_EUNSUPPORTED;
+  return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cache, const int32_t* block_tables,
+               const int32_t* seq_lens, const int32_t* query_start_loc, const pa_shape* shape,
+               int32_t num_query_tokens, int32_t max_query_len, float scale, void* stream) {
+  const int st = check_prefill(out, q, k_cache, v_cache, block_tables, seq_lens, query_start_loc, shape,
+                               num_query_tokens, max_query_len);
+  if (st != PA_OK) return st;
+  const Launch L = on(stream);
+  if (shape->num_seqs == 0 || num_query_tokens == 0 || max_query_len == 0)
+    return nothing_launched(L) == hipSuccess ? PA_OK : PA_EHIP;
+  (void)hipGetLastError();
+  PrefillParams P;
+  P.q = q; P.k = k_cache; P.v = v_cache; P.bt = block_tables; P.sl = seq_lens; P.qsl = query_start_loc;
+  P.out = out; P.NB = shape->num_blocks;
+  P.S = shape->num_seqs; P.H = shape->num_heads; P.Hkv = shape->num_kv_heads;
+  P.G = shape->num_heads / shape->num_kv_heads; P.MB = shape->max_blocks_per_seq;
+  P.T = num_query_tokens; P.QT = kPrefillRows / P.G;
+  P.scale2 = scale * kLog2e;
+  const int nqt = (max_query_len + P.QT - 1) / P.QT;
+  const hipError_t e = shape->dtype == PA_BF16 ? launch_prefill_t<__bf16>(P, shape->head_dim, nqt, L)
+                                               : launch_prefill_t<_Float16>(P, shape->head_dim, nqt, L);
+  return e == hipSuccess ? PA_OK : PA_EHIP;
+}
+
+}  // extern "C"
