@@ -21,12 +21,49 @@ namespace {
 // head, so one K/V tile serves every head of the group and QT tokens. One
 // workgroup takes (sequence, KV head, QT-token query tile); each of its NW
 // waves owns NTW N-tiles of 16 rows and walks every key tile itself (no merge
-// across waves). K/V tiles are read with cacheable loads: the workgroup's
-// waves read the same tiles at about the same time and share them through
-// the L1/L2. K goes through the wave-private swizzled LDS tile; V is
-// transposed in registers; P is the QK accumulator rounded to the 16-bit
-// type. Outputs are stored straight from the accumulators (8 consecutive dims
-// per 16-byte store).
+// across waves). In the shared form (head_dim 128) the workgroup stages each
+// K/V tile once into one of two LDS buffers (K XOR-swizzled by row so the
+// token-wise operand reads hit distinct banks), with the loads of the next
+// SHD tiles already in flight in registers; every wave reads its operands
+// there. In the per-wave form (head_dim 256) each wave loads its own tile and
+// passes K through a wave-private swizzled LDS tile. V is transposed in
+// registers; P is the QK accumulator rounded to the 16-bit type. Outputs are
+// stored straight from the accumulators (8 consecutive dims per 16-byte
+// store).
+// Max and sum over the four lane groups (lanes l, l^16, l^32, l^48: the same
+// row) with the gfx950 lane-swap moves instead of LDS-routed shuffles.
+// v_permlane16_swap a, b exchanges rows 1/3 of a with rows 0/2 of b; with b a
+// copy of a, lane l then holds v[l] and v[l^16] across a and b, and
+// v_permlane32_swap pairs l with l^32 the same way. The max (or the sum, which
+// is commutative) of a and b is then the same value in both lanes of a pair.
+// Written as inline assembly with both registers read-write: the compiler's
+// builtin for these swaps returned the first result in place of the second
+// when both inputs held the same value. The s_nop pairs cover the VALU ->
+// lane-swap -> VALU data hazards.
+#ifndef PA_PREFILL_PERMLANE
+#define PA_PREFILL_PERMLANE 1
+#endif
+template <bool SUM>
+__device__ __forceinline__ float rows_reduce(float x) {
+  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  const float a0 = __builtin_bit_cast(float, a), a1 = __builtin_bit_cast(float, b);
+  x = SUM ? a0 + a1 : fmaxf(a0, a1);
+  a = __builtin_bit_cast(uint32_t, x);
+  b = a;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+  const float b0 = __builtin_bit_cast(float, a), b1 = __builtin_bit_cast(float, b);
+  return SUM ? b0 + b1 : fmaxf(b0, b1);
+}
+__device__ __forceinline__ float rows_max(float x) {
+  if constexpr (PA_PREFILL_PERMLANE) return rows_reduce<false>(x);
+  return group_max(x);
+}
+__device__ __forceinline__ float rows_sum(float x) {
+  if constexpr (PA_PREFILL_PERMLANE) return rows_reduce<true>(x);
+  return group_sum(x);
+}
+
 struct PrefillParams {
   const void* q;
   const void* k;
@@ -40,7 +77,7 @@ struct PrefillParams {
   float scale2;
 };
 
-template <typename T, int D, int NW, int NTW, int TB, bool PF>
+template <typename T, int D, int NW, int NTW, int TB, bool SH, int SHD>
 __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   typedef typename H16<T>::x8 tx8;
   typedef typename H16<T>::x4 tx4;
@@ -156,27 +193,8 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     issue_tile<T, D, TB, false>(tl, kbase, vbase, block_elems, phys, vb, g, grp);
   };
 
-  auto compute = [&](BTile<D, TB>& tl, int t) {
-
-    // K: registers -> swizzled LDS tile -> MFMA A operands.
-#pragma unroll
-    for (int b = 0; b < TB; ++b)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          const int row = 4 * grp + rr, c16 = 16 * h + g;
-          ktile[(b * 16 + row) * KCH + (c16 ^ row)] = tl.k[b][rr][h];
-        }
-    tx8 ka[TB][KK];
-#pragma unroll
-    for (int b = 0; b < TB; ++b)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int c16 = 4 * kk + grp;
-        ka[b][kk] = __builtin_bit_cast(tx8, ktile[(b * 16 + g) * KCH + (c16 ^ g)]);
-      }
-
+  // The math of tile t: K as MFMA A operands (ka), V as raw rows (tl.v).
+  auto compute_ops = [&](tx8 (&ka)[TB][KK], BTile<D, TB>& tl, int t) {
     const int tok0 = t * TB * kBS;
     // V rows at or past kmax (tail slots of the last block, blocks past the
     // end) are zeroed: a zero weight times NaN would poison the sum.
@@ -210,7 +228,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
           x[b][i] = z;
           mx = fmaxf(mx, z);
         }
-      mx = group_max(mx);
+      mx = rows_max(mx);
       const float mnew = fmaxf(m[jj], mx);  // finite: key 0 is in every row's first tile
       const float alpha = fast_exp2(m[jj] - mnew);
       m[jj] = mnew;
@@ -277,22 +295,120 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     }
   };
 
-  BTile<D, TB> A;
-  issue(A, 0);
-  if constexpr (PF) {
-    // Two register stages: the next tile's loads are in flight while this
-    // tile's math runs (a workgroup's waves are few per SIMD here).
-    BTile<D, TB> B;
-    for (int t = 0;;) {
-      if (t + 1 < ntiles) issue(B, t + 1);
-      compute(A, t);
-      if (t + 1 >= ntiles) break;
-      if (t + 2 < ntiles) issue(A, t + 2);
-      compute(B, t + 1);
-      if (t + 2 >= ntiles) break;
-      t += 2;
+  // Per-wave path: the wave's own K tile goes registers -> its LDS tile ->
+  // MFMA A operands.
+  auto compute = [&](BTile<D, TB>& tl, int t) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+        for (int h = 0; h < NH; ++h) {
+          const int row = 4 * grp + rr, c16 = 16 * h + g;
+          ktile[(b * 16 + row) * KCH + (c16 ^ row)] = tl.k[b][rr][h];
+        }
+    tx8 ka[TB][KK];
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) {
+        const int c16 = 4 * kk + grp;
+        ka[b][kk] = __builtin_bit_cast(tx8, ktile[(b * 16 + g) * KCH + (c16 ^ g)]);
+      }
+    compute_ops(ka, tl, t);
+  };
+
+  if constexpr (SH) {
+    // Shared path: the workgroup loads each K/V tile once, 16 bytes per
+    // thread-chunk, into one of two LDS stages (K XOR-swizzled by row as
+    // above, V row-major); every wave reads its MFMA operands from there.
+    // The next tile's chunks are in registers while this tile's math runs;
+    // one barrier per tile publishes the next stage.
+    constexpr int TCH = TB * 16 * KCH;               // 16-byte chunks of K (or V) per tile
+    constexpr int PER = 2 * TCH / (NW * 64);         // chunks per thread per tile
+    static_assert(PER * NW * 64 == 2 * TCH, "tile chunks must split evenly over the threads");
+    u32x4* kst = reinterpret_cast<u32x4*>(smem);     // [2][TCH]
+    u32x4* vst = kst + 2 * TCH;                      // [2][TCH]
+    auto fetch = [&](u32x4 (&stage)[PER], int t) {
+      if (t % CH == 0) refill(t / CH);
+      int64_t phys[TB];
+      bool vb[TB];
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        vb[b] = t * TB + b < nblk;
+        phys[b] = __builtin_amdgcn_readlane(ids, (t % CH) * TB + b);
+      }
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int id = u * NW * 64 + (int)threadIdx.x;
+        const int kv = id / TCH, r = id % TCH;
+        const int b = r / (16 * KCH), row = (r / KCH) % 16, c = r % KCH;
+        int64_t pb = phys[0];
+        bool ok = vb[0];
+#pragma unroll
+        for (int bb = 1; bb < TB; ++bb)
+          if (b == bb) {
+            pb = phys[bb];
+            ok = vb[bb];
+          }
+        const T* src = (kv ? vbase : kbase) + pb * block_elems + row * D + c * 8;
+        stage[u] = ok ? ld16(src) : (u32x4){0u, 0u, 0u, 0u};
+      }
+    };
+    auto deposit = [&](const u32x4 (&stage)[PER], int buf) {
+#pragma unroll
+      for (int u = 0; u < PER; ++u) {
+        const int id = u * NW * 64 + (int)threadIdx.x;
+        const int kv = id / TCH, r = id % TCH;
+        const int b = r / (16 * KCH), row = (r / KCH) % 16, c = r % KCH;
+        if (kv == 0)
+          kst[buf * TCH + (b * 16 + row) * KCH + (c ^ row)] = stage[u];
+        else
+          vst[buf * TCH + (b * 16 + row) * KCH + c] = stage[u];
+      }
+    };
+    // SHD register stages: tile t's slot is t % SHD. At the top of iteration
+    // t that slot is free (tile t went to LDS in iteration t - 1) and takes
+    // the loads of tile t + SHD, which then have SHD tiles of math to arrive
+    // in; after the math, tile t + 1 goes from its slot to the other LDS
+    // stage. The loop runs in groups of SHD so every slot index is a
+    // compile-time constant.
+    u32x4 stage[SHD][PER];
+#pragma unroll
+    for (int d = 0; d < SHD; ++d)
+      if (d < ntiles) fetch(stage[d], d);
+    deposit(stage[0], 0);
+    __syncthreads();
+    BTile<D, TB> tl;
+    for (int t0 = 0; t0 < ntiles; t0 += SHD) {
+#pragma unroll
+    for (int d = 0; d < SHD; ++d) {
+      const int t = t0 + d;
+      if (t >= ntiles) break;
+      const int buf = t & 1;
+      // slot d held tile t, already in LDS: refill it with tile t + SHD
+      if (t + SHD < ntiles) fetch(stage[d], t + SHD);
+      tx8 ka[TB][KK];
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+          const int c16 = 4 * kk + grp;
+          ka[b][kk] = __builtin_bit_cast(tx8, kst[buf * TCH + (b * 16 + g) * KCH + (c16 ^ g)]);
+        }
+#pragma unroll
+        for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+          for (int h = 0; h < NH; ++h) tl.v[b][rr][h] = vst[buf * TCH + (b * 16 + 4 * grp + rr) * KCH + 16 * h + g];
+      }
+      compute_ops(ka, tl, t);
+      if (t + 1 < ntiles) deposit(stage[(d + 1) % SHD], buf ^ 1);
+      __syncthreads();
+    }
     }
   } else {
+    BTile<D, TB> A;
+    issue(A, 0);
     for (int t = 0;;) {
       compute(A, t);
       if (++t >= ntiles) break;
@@ -304,7 +420,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   // for fixed (h, i) the 8 values j = 0..7 are consecutive dims.
 #pragma unroll
   for (int jj = 0; jj < NTW; ++jj) {
-    const float tot = group_sum(lsum[jj]);
+    const float tot = rows_sum(lsum[jj]);
     if (!valid[jj]) continue;
     const float inv = live[jj] ? 1.f / tot : 0.f;
     T* orow = out_row(jj);
@@ -320,34 +436,43 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   }
 }
 
-// Prefill launch shape: 128 query rows per workgroup (QT tokens x G heads).
-// D=128, at most kPrefillSmallGrid workgroups (one or two per CU, long
-// contexts): 8 waves x 1 N-tile, two-block tiles, next tile prefetched into
-// registers, since few waves share a SIMD; larger grids: 4 waves x 2 N-tiles,
-// one-block tiles, no prefetch (2 waves per SIMD resident). D=256: 8 waves x 1
-// N-tile, one-block tiles (register budget). Measured on the four prefill
-// workloads against the other combinations of these knobs.
-constexpr int kPrefillRows = 128;
-constexpr int kPrefillMaxNW = 8;  // waves per workgroup, largest launch shape
+// Prefill launch shapes (measured on the four prefill workloads against the
+// other combinations of waves, N-tiles per wave, tile blocks, prefetch depth
+// and shared/per-wave tiles):
+//   D = 128, at most kPrefillSmallGrid workgroups of 128 rows (long contexts,
+//     few query tiles): 8 waves x 1 N-tile, two-block tiles shared through
+//     LDS, 4 register stages of prefetch;
+//   D = 128, larger grids: 256 rows per workgroup, 8 waves x 2 N-tiles (half
+//     the LDS operand traffic per row), 2 stages;
+//   D = 256: 128 rows, 8 waves x 1 N-tile, per-wave one-block tiles (the
+//     register budget of the wider rows).
+constexpr int kPrefillRows = 128;      // rows per workgroup of the smallest shape
+constexpr int kPrefillMaxNW = 8;       // waves per workgroup, largest launch shape
 constexpr int64_t kPrefillSmallGrid = 512;
 
 template <typename T>
-hipError_t launch_prefill_t(const PrefillParams& P, int D, int nqt, const Launch& L) {
-  const dim3 grid((unsigned)((int64_t)P.S * P.Hkv * nqt));
-  if (grid.x == 0) return nothing_launched(L);
+hipError_t launch_prefill_t(PrefillParams P, int D, int maxq, const Launch& L) {
+  const int64_t pairs = (int64_t)P.S * P.Hkv;
+  auto tiles = [&](int rows) { const int qt = rows / P.G; return pairs * ((maxq + qt - 1) / qt); };
   if (D == 128) {
-    if ((int64_t)grid.x <= kPrefillSmallGrid) {
+    if (tiles(128) <= kPrefillSmallGrid) {
       constexpr int NW = 8, NTW = 1, TB = 2;
-      const size_t smem = (size_t)NW * TB * 16 * 128 * sizeof(T);
-      return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true>, grid, dim3(NW * 64), smem, L, P);
+      P.QT = 128 / P.G;
+      const size_t smem = (size_t)4 * TB * 16 * 128 * sizeof(T);  // two stages of K and V
+      return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true, 4>, dim3((unsigned)tiles(128)), dim3(NW * 64), smem,
+                    L, P);
     }
-    constexpr int NW = 4, NTW = 2, TB = 1;
-    const size_t smem = (size_t)NW * TB * 16 * 128 * sizeof(T);
-    return launch(pa_prefill_h16<T, 128, NW, NTW, TB, false>, grid, dim3(NW * 64), smem, L, P);
+    constexpr int NW = 8, NTW = 2, TB = 2;
+    P.QT = 256 / P.G;
+    const size_t smem = (size_t)4 * TB * 16 * 128 * sizeof(T);
+    return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true, 2>, dim3((unsigned)tiles(256)), dim3(NW * 64), smem, L,
+                  P);
   }
   constexpr int NW = 8, NTW = 1, TB = 1;
+  P.QT = 128 / P.G;
   const size_t smem = (size_t)NW * TB * 16 * 256 * sizeof(T);
-  return launch(pa_prefill_h16<T, 256, NW, NTW, TB, false>, grid, dim3(NW * 64), smem, L, P);
+  return launch(pa_prefill_h16<T, 256, NW, NTW, TB, false, 1>, dim3((unsigned)tiles(128)), dim3(NW * 64), smem, L,
+                P);
 }
 
 int check_prefill(const void* out, const void* q, const void* k, const void* v, const int32_t* bt,
@@ -388,11 +513,11 @@ int pa_prefill(void* out, const void* q, const void* k_cache, const void* v_cach
   P.out = out; P.NB = shape->num_blocks;
   P.S = shape->num_seqs; P.H = shape->num_heads; P.Hkv = shape->num_kv_heads;
   P.G = shape->num_heads / shape->num_kv_heads; P.MB = shape->max_blocks_per_seq;
-  P.T = num_query_tokens; P.QT = kPrefillRows / P.G;
+  P.T = num_query_tokens;
+  P.QT = 0;  // set by the launch shape
   P.scale2 = scale * kLog2e;
-  const int nqt = (max_query_len + P.QT - 1) / P.QT;
-  const hipError_t e = shape->dtype == PA_BF16 ? launch_prefill_t<__bf16>(P, shape->head_dim, nqt, L)
-                                               : launch_prefill_t<_Float16>(P, shape->head_dim, nqt, L);
+  const hipError_t e = shape->dtype == PA_BF16 ? launch_prefill_t<__bf16>(P, shape->head_dim, max_query_len, L)
+                                               : launch_prefill_t<_Float16>(P, shape->head_dim, max_query_len, L);
   return e == hipSuccess ? PA_OK : PA_EHIP;
 }
 

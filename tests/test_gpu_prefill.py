@@ -200,3 +200,14 @@ def test_prefill_large_grid_every_token(dev):
     x = W.make_prefill_inputs(W.PREFILL_CONFIGS[2], seed=58, context_lens=ctx, query_lens=ql)
     say(f"prefill large grid: {S} seqs, {x.num_query_tokens} tokens")
     check_all(x, run(x, dev), "large grid")
+
+
+def test_prefill_large_grid_odd_group(dev):
+    """The 256-row launch shape with G = 3 (85 tokens x 3 heads = 255 rows per tile), every token."""
+    rng = np.random.default_rng(59)
+    S = 40
+    cfg = W.PrefillConfig("g3", S, 12, 4, 128, "bf16", ("custom",), ("custom",))
+    x = W.make_prefill_inputs(cfg, seed=59, context_lens=rng.integers(0, 200, size=S),
+                              query_lens=rng.integers(150, 201, size=S))
+    say(f"prefill large grid, G=3: {x.num_query_tokens} tokens")
+    check_all(x, run(x, dev), "large grid G=3")
