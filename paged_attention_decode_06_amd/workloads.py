@@ -59,7 +59,7 @@ class DecodeConfig:
 
 
 # The five decode workloads (seed = 1000 + number).
-CONFIGS = {
+DECODE_WORKLOADS = {
     1: DecodeConfig("tiny-L37-fp32", 1, 2, 1, 128, "f32", ("fixed", 37), pool_blocks=64),
     2: DecodeConfig("batch8-U1-8192-bf16", 8, 16, 2, 128, "bf16", ("uniform", 1, 8192)),
     3: DecodeConfig("ctx100K-bf16", 1, 16, 2, 128, "bf16", ("fixed", 100000)),
@@ -205,7 +205,7 @@ def make_inputs(cfg: DecodeConfig | int, seed: int | None = None, *, seq_lens=No
     number = None
     if isinstance(cfg, int):
         number = cfg
-        cfg = CONFIGS[cfg]
+        cfg = DECODE_WORKLOADS[cfg]
     if seed is None:
         seed = 1000 + (number if number is not None else 0)
     trng = _rng(seed, _PURPOSE_TABLE)
@@ -288,7 +288,7 @@ class PrefillConfig:
 # the same mix at head_dim 256. Chunked prefill with 8K-32K batched tokens and
 # 100K contexts is the serving setting the pages describe (prefix_prefill_patch.py
 # docstring, yaml analysis; commit 490ff98a, computility-run.yaml change).
-PREFILL_CONFIGS = {
+PREFILL_WORKLOADS = {
     1: PrefillConfig("chunk2048-ctx100K-bf16", 1, 16, 2, 128, "bf16", ("fixed", 100000 - 2048), ("fixed", 2048)),
     2: PrefillConfig("batch16-prompt1024-bf16", 16, 16, 2, 128, "bf16", ("fixed", 0), ("fixed", 1024)),
     3: PrefillConfig("batch8-ctxU0-32768-chunkU1-2048-bf16", 8, 16, 2, 128, "bf16",
@@ -346,7 +346,7 @@ def make_prefill_inputs(cfg: PrefillConfig | int, seed: int | None = None, *, co
     number = None
     if isinstance(cfg, int):
         number = cfg
-        cfg = PREFILL_CONFIGS[cfg]
+        cfg = PREFILL_WORKLOADS[cfg]
     if seed is None:
         seed = 2000 + (number if number is not None else 0)
     trng = _rng(seed, _PURPOSE_TABLE)
@@ -418,7 +418,7 @@ class MoeConfig:
 # 256 experts with top 8 (the pages' MoE rewrite); 16384 tokens is the
 # prefill batch the same passage sizes; 256 tokens a decode step at 256
 # concurrent sequences. Hidden size 2048 is a stand-in (the pages give none).
-MOE_CONFIGS = {
+MOE_WORKLOADS = {
     1: MoeConfig("prefill-T16384-E256-k8-H2048-bf16", 16384, 256, 8, 2048),
     2: MoeConfig("decode-T256-E256-k8-H2048-bf16", 256, 256, 8, 2048),
 }
@@ -439,7 +439,7 @@ def make_moe_inputs(cfg: MoeConfig | int, seed: int | None = None, *, num_tokens
     number = None
     if isinstance(cfg, int):
         number = cfg
-        cfg = MOE_CONFIGS[cfg]
+        cfg = MOE_WORKLOADS[cfg]
     if num_tokens is not None:
         cfg = MoeConfig(cfg.name + "-custom", int(num_tokens), cfg.num_experts, cfg.top_k, cfg.hidden,
                         cfg.dtype, cfg.renormalize)

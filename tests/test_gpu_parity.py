@@ -211,7 +211,7 @@ def test_poison_outside_contexts_never_reaches_output(dev, dtype, mode, width):
 
 # ---------------------------------------------------------------- invariants
 def test_block_permutation_is_bitwise_invariant(dev):
-    x = W.make_inputs(W.CONFIGS[2], seed=17, seq_lens=[37, 4000, 9000, 20000])
+    x = W.make_inputs(W.DECODE_WORKLOADS[2], seed=17, seq_lens=[37, 4000, 9000, 20000])
     say("block permutation")
     base = W.from_device(run(x, dev, "auto")[0])
     rng = np.random.default_rng(0)
@@ -224,7 +224,7 @@ def test_block_permutation_is_bitwise_invariant(dev):
 
 
 def test_runs_are_bitwise_deterministic(dev):
-    x = W.make_inputs(W.CONFIGS[2], seed=18, seq_lens=[100, 8192, 30000])
+    x = W.make_inputs(W.DECODE_WORKLOADS[2], seed=18, seq_lens=[100, 8192, 30000])
     d = W.to_device(x, dev)
     say("determinism")
     a = W.from_device(run(x, dev, "auto", d)[0])
@@ -247,7 +247,7 @@ def test_single_token_returns_v_exactly(dev, dtype):
 
 @pytest.mark.parametrize("mode", MODES)
 def test_constant_v_gives_the_constant(dev, mode):
-    x = W.make_inputs(W.CONFIGS[2], seed=20, seq_lens=[37, 8192, 9000, 20000])
+    x = W.make_inputs(W.DECODE_WORKLOADS[2], seed=20, seq_lens=[37, 8192, 9000, 20000])
     x.v_cache[:] = W.f32_to_bf16_bits(np.full(1, 1.625, np.float32))[0]
     say(f"constant V mode={mode}")
     got = W.from_device(run(x, dev, mode)[0])
@@ -255,7 +255,7 @@ def test_constant_v_gives_the_constant(dev, mode):
 
 
 def test_zero_query_gives_mean_of_v(dev):
-    x = W.make_inputs(W.CONFIGS[2], seed=21, seq_lens=[37, 3000, 9000])
+    x = W.make_inputs(W.DECODE_WORKLOADS[2], seed=21, seq_lens=[37, 3000, 9000])
     x.q[:] = 0
     say("zero query")
     out, _ = run(x, dev, "auto")
@@ -272,7 +272,7 @@ def test_zero_query_gives_mean_of_v(dev):
 @pytest.mark.parametrize("mode", MODES)
 def test_gather_trace_matches_oracle_exactly(dev, mode, width):
     lens = [37, 1, 8192, 8193, 20000, 513, 40000, 9000]
-    x = W.make_inputs(W.CONFIGS[2], seed=22, seq_lens=lens, max_blocks_per_seq=max(width, 2500), poison=True)
+    x = W.make_inputs(W.DECODE_WORKLOADS[2], seed=22, seq_lens=lens, max_blocks_per_seq=max(width, 2500), poison=True)
     d = W.to_device(x, dev)
     sh = pa.make_shape(d["q"], d["k_cache"], d["block_tables"])
     es, ml, to = pa.alloc_partials(sh, dev)
@@ -295,7 +295,7 @@ def test_gather_trace_matches_oracle_exactly(dev, mode, width):
 @pytest.mark.parametrize("width", WIDTHS)
 def test_partials_match_oracle_partition_stats(dev, width, ps):
     lens = [1100, 513, 9000, 1, 257]
-    x = W.make_inputs(W.CONFIGS[2], seed=23, seq_lens=lens, max_blocks_per_seq=width)
+    x = W.make_inputs(W.DECODE_WORKLOADS[2], seed=23, seq_lens=lens, max_blocks_per_seq=width)
     d = W.to_device(x, dev)
     sh = pa.make_shape(d["q"], d["k_cache"], d["block_tables"], ps)
     es, ml, to = pa.alloc_partials(sh, dev)
@@ -352,7 +352,7 @@ def test_reduce_fed_with_oracle_partials(dev, dtype, S, H, D, ps):
 @pytest.mark.parametrize("width", WIDTHS)
 def test_auto_writes_partials_only_for_long_contexts(dev, width):
     lens = [37, 8192, 8193, 20000, 600]
-    x = W.make_inputs(W.CONFIGS[2], seed=25, seq_lens=lens, max_blocks_per_seq=width)
+    x = W.make_inputs(W.DECODE_WORKLOADS[2], seed=25, seq_lens=lens, max_blocks_per_seq=width)
     d = W.to_device(x, dev)
     sh = pa.make_shape(d["q"], d["k_cache"], d["block_tables"])
     es, ml, to = pa.alloc_partials(sh, dev)
@@ -374,7 +374,7 @@ def test_auto_writes_partials_only_for_long_contexts(dev, width):
 
 
 def test_data_errors_are_flagged_not_faulted(dev):
-    x = W.make_inputs(W.CONFIGS[2], seed=26, seq_lens=[40, 40])
+    x = W.make_inputs(W.DECODE_WORKLOADS[2], seed=26, seq_lens=[40, 40])
     x.block_tables[1, 1] = x.num_blocks + 5          # out of the pool
     x.seq_lens[0] = 40 + 16 * x.max_blocks_per_seq    # longer than the table
     d = W.to_device(x, dev)
@@ -393,7 +393,7 @@ def test_data_errors_are_flagged_not_faulted(dev):
 def test_timed_entry_points_match_untimed(dev, mode):
     """The *_timed forms run the same kernels: bitwise equal outputs, and both
     event pairs complete (also where the reduce has nothing to launch)."""
-    x = W.make_inputs(W.CONFIGS[2], seed=19, seq_lens=[5, 3000, 8192, 8193, 40000])
+    x = W.make_inputs(W.DECODE_WORKLOADS[2], seed=19, seq_lens=[5, 3000, 8192, 8193, 40000])
     d = W.to_device(x, dev)
     say(f"timed entry points, mode {mode}")
     m = {"auto": pa.MODE_AUTO, "v1": pa.MODE_V1, "v2": pa.MODE_V2}[mode]
@@ -426,7 +426,7 @@ def test_timed_entry_points_match_untimed(dev, mode):
 
 
 def test_timed_entry_points_on_an_empty_batch(dev):
-    x = W.make_inputs(W.CONFIGS[2], seed=20, seq_lens=[7])
+    x = W.make_inputs(W.DECODE_WORKLOADS[2], seed=20, seq_lens=[7])
     d = W.to_device(x, dev)
     q0 = d["q"][:0]
     out = torch.empty_like(q0)
@@ -470,7 +470,7 @@ def test_modes_vs_oracle_partition_256(dev, D, mode, width, dtype):
 @pytest.mark.parametrize("mode", ["auto", "v2"])
 def test_gather_trace_partition_256(dev, mode):
     lens = [300, 4000, 9000]
-    x = W.make_inputs(W.CONFIGS[2], seed=32, seq_lens=lens, max_blocks_per_seq=1300)
+    x = W.make_inputs(W.DECODE_WORKLOADS[2], seed=32, seq_lens=lens, max_blocks_per_seq=1300)
     d = W.to_device(x, dev)
     sh = pa.make_shape(d["q"], d["k_cache"], d["block_tables"], 256)
     es, ml, to = pa.alloc_partials(sh, dev)
@@ -490,7 +490,7 @@ def test_gather_trace_partition_256(dev, mode):
 
 
 def test_partition_256_and_512_agree(dev):
-    x = W.make_inputs(W.CONFIGS[2], seed=33, seq_lens=[9000, 30000, 100])
+    x = W.make_inputs(W.DECODE_WORKLOADS[2], seed=33, seq_lens=[9000, 30000, 100])
     d = W.to_device(x, dev)
     say("256 vs 512 partitions")
     a = W.from_device(run(x, dev, "v2", d)[0])

@@ -170,7 +170,7 @@ def test_prefill_empty_inputs(dev):
 
 
 def test_prefill_block_permutation_bitwise_and_deterministic(dev):
-    x = W.make_prefill_inputs(W.PREFILL_CONFIGS[2], seed=56, context_lens=[700, 40], query_lens=[300, 90])
+    x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=56, context_lens=[700, 40], query_lens=[300, 90])
     say("prefill block permutation / determinism")
     a = W.from_device(run(x, dev))
     b = W.from_device(run(x, dev))
@@ -197,7 +197,7 @@ def test_prefill_large_grid_every_token(dev):
     S = 40
     ctx = rng.integers(0, 300, size=S)
     ql = rng.integers(100, 129, size=S)
-    x = W.make_prefill_inputs(W.PREFILL_CONFIGS[2], seed=58, context_lens=ctx, query_lens=ql)
+    x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=58, context_lens=ctx, query_lens=ql)
     say(f"prefill large grid: {S} seqs, {x.num_query_tokens} tokens")
     check_all(x, run(x, dev), "large grid")
 

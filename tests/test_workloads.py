@@ -64,7 +64,7 @@ def test_generation_is_deterministic():
 
 def test_loguniform_lengths_in_range():
     rng = np.random.default_rng(0)
-    lens = W.draw_seq_lens(W.CONFIGS[4], rng)
+    lens = W.draw_seq_lens(W.DECODE_WORKLOADS[4], rng)
     assert lens.min() >= 512 and lens.max() <= 65536 and lens.size == 64
 
 
@@ -105,8 +105,8 @@ def test_algorithmic_bytes_long_context():
 
 # ---------------------------------------------------------------- prefill inputs
 def test_prefill_inputs_are_consistent_and_seeded():
-    for k in W.PREFILL_CONFIGS:
-        cfg = W.PREFILL_CONFIGS[k]
+    for k in W.PREFILL_WORKLOADS:
+        cfg = W.PREFILL_WORKLOADS[k]
         if k == 1:
             continue   # the 100K one is exercised by the GPU tests; shape arithmetic below covers it
         x = W.make_prefill_inputs(k)
@@ -124,13 +124,13 @@ def test_prefill_inputs_are_consistent_and_seeded():
 
 
 def test_prefill_overrides_and_flops():
-    x = W.make_prefill_inputs(W.PREFILL_CONFIGS[2], seed=5, context_lens=[0, 10, 100], query_lens=[7, 1, 33])
+    x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=5, context_lens=[0, 10, 100], query_lens=[7, 1, 33])
     assert list(x.seq_lens) == [7, 11, 133] and list(x.query_start_loc) == [0, 7, 8, 41]
     assert x.max_query_len == 33 and x.num_query_tokens == 41
     # keys seen: 1..7, 11, 101..133
     keys = sum(range(1, 8)) + 11 + sum(range(101, 134))
     assert W.prefill_flops(x.seq_lens, x.query_lens, 16, 128) == 4 * 128 * 16 * keys
-    p = W.make_prefill_inputs(W.PREFILL_CONFIGS[2], seed=5, context_lens=[3], query_lens=[20], poison=True)
+    p = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=5, context_lens=[3], query_lens=[20], poison=True)
     assert p.k_cache.shape[0] == p.num_blocks and p.extra["poison_block"] == p.num_blocks - 1
 
 
