@@ -462,7 +462,7 @@ def bench_moe(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
     stages = [
         ("topk_softmax", lambda: pa.pa_moe_topk_softmax(w, ids, logits, c.renormalize, stream=stream)),
         ("sort_by_expert", lambda: pa.pa_moe_sort_by_expert(sp, pp, off, ids, E, ws, stream=stream)),
-        ("permute", lambda: pa.pa_moe_permute(xs, xh, sp, K, stream=stream)),
+        ("permute", lambda: pa.pa_moe_permute(xs, xh, pp, K, stream=stream)),
         ("combine", lambda: pa.pa_moe_combine(out, ys, w, pp, stream=stream)),
     ]
     for _ in range(warmup):

@@ -70,13 +70,19 @@ int pa_moe_sort_by_expert(int32_t* sorted_pairs, int32_t* pair_pos, int32_t* exp
                           const int32_t* topk_ids, int32_t T, int32_t E, int32_t K, void* workspace,
                           int64_t workspace_bytes, void* stream);
 
-/* Gather the expert inputs into sorted order ([cd0d9e1a] MoE rewrite, step 3:
- * contiguous rows per expert): x_sorted[i, :] = x[sorted_pairs[i] / K, :].
+/* Lay the expert inputs out in sorted order ([cd0d9e1a] MoE rewrite, step 3:
+ * contiguous rows per expert): x_sorted[pair_pos[t*K + j], :] = x[t, :] for
+ * every token t and choice j; with pair_pos from pa_moe_sort_by_expert this is
+ * x_sorted[i, :] = x[sorted_pairs[i] / K, :]. Done token-major: each row of x
+ * is read once and written to its K positions.
  *   x         [T, hidden]     dtype (pa_dtype of pa_decode.h: f32, bf16, f16)
+ *   pair_pos  int32 [T*K]     a permutation of 0..T*K-1 (if it is not, rows
+ *                             that two pairs name get either one's row and
+ *                             rows no pair names are left as they were)
  *   x_sorted  [T*K, hidden]   dtype; hidden * element size must be a
  *                             multiple of 16 bytes                        */
-int pa_moe_permute(void* x_sorted, const void* x, const int32_t* sorted_pairs, int32_t T, int32_t K,
-                   int32_t hidden, int32_t dtype, void* stream);
+int pa_moe_permute(void* x_sorted, const void* x, const int32_t* pair_pos, int32_t T, int32_t K, int32_t hidden,
+                   int32_t dtype, void* stream);
 
 /* Weighted scatter-back of the expert outputs ([cd0d9e1a] MoE rewrite, step
  * 5, the index_add_): out[t, :] = sum_{j<K} topk_weights[t, j] *

@@ -330,13 +330,13 @@ def pa_moe_sort_by_expert(sorted_pairs, pair_pos, expert_offsets, topk_ids, num_
         _ptr(workspace), int(nbytes), _stream(stream, topk_ids.device)))
 
 
-def pa_moe_permute(x_sorted, x, sorted_pairs, top_k, stream=None):
-    """x [T, hidden] -> x_sorted [T*K, hidden]: row i = x[sorted_pairs[i] // K]."""
-    _gpu_contig(x_sorted, x, sorted_pairs)
+def pa_moe_permute(x_sorted, x, pair_pos, top_k, stream=None):
+    """x [T, hidden] -> x_sorted [T*K, hidden]: row pair_pos[t*K + j] = x[t]."""
+    _gpu_contig(x_sorted, x, pair_pos)
     T, Hd = x.shape
-    if tuple(x_sorted.shape) != (T * top_k, Hd) or x_sorted.dtype != x.dtype or sorted_pairs.numel() != T * top_k:
-        raise PaError(PA_EINVAL, "x_sorted must be [T*K, hidden] of x's dtype; sorted_pairs T*K entries")
-    _call("pa_moe_permute", load().pa_moe_permute(_ptr(x_sorted), _ptr(x), _ptr(sorted_pairs), T, int(top_k), Hd,
+    if tuple(x_sorted.shape) != (T * top_k, Hd) or x_sorted.dtype != x.dtype or pair_pos.numel() != T * top_k:
+        raise PaError(PA_EINVAL, "x_sorted must be [T*K, hidden] of x's dtype; pair_pos T*K entries")
+    _call("pa_moe_permute", load().pa_moe_permute(_ptr(x_sorted), _ptr(x), _ptr(pair_pos), T, int(top_k), Hd,
                                                   _dtype_code(x.dtype), _stream(stream, x.device)))
 
 

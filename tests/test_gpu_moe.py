@@ -111,19 +111,23 @@ def test_sort_out_of_range_ids_stay_in_bounds(dev):
     assert np.array_equal(sp, osp) and np.array_equal(pp, opp) and np.array_equal(off, ooff)
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f32", "f16"])
-def test_permute_is_an_exact_gather(dev, dtype):
-    cfg = W.MoeConfig("perm", 300, 64, 4, 256, dtype)
+@pytest.mark.parametrize("T,E,K,hidden,dtype", [(300, 64, 4, 256, "bf16"), (300, 64, 4, 256, "f32"),
+                                                 (300, 64, 4, 256, "f16"), (77, 256, 32, 2056, "bf16"),
+                                                 (1000, 16, 1, 3000, "f16"), (5, 8, 8, 4100, "f32")])
+def test_permute_is_exact(dev, T, E, K, hidden, dtype):
+    """Every sorted row is the oracle's (written exactly once: the buffer starts as a sentinel); rows
+    longer than one 4 KB pass and ragged last slices included."""
+    cfg = W.MoeConfig("perm", T, E, K, hidden, dtype)
     x = W.make_moe_inputs(cfg, seed=5)
-    rng = np.random.default_rng(5)
-    ids = rng.integers(0, 64, size=(300, 4)).astype(np.int32)
-    osp, _, _ = om.sort_by_expert(ids, 64)
-    xs = torch.empty((1200, 256), dtype=to_dev(x.x[:1], dev).dtype, device=dev)
-    say(f"permute {dtype}")
-    pa.pa_moe_permute(xs, to_dev(x.x, dev), torch.from_numpy(osp).to(dev), 4)
+    rng = np.random.default_rng(T + K)
+    ids = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    osp, opp, _ = om.sort_by_expert(ids, E)
+    xs = torch.full((T * K, hidden), 7.0, dtype=to_dev(x.x[:1], dev).dtype, device=dev)
+    say(f"permute T={T} E={E} K={K} hidden={hidden} {dtype}")
+    pa.pa_moe_permute(xs, to_dev(x.x, dev), torch.from_numpy(opp).to(dev), K)
     torch.cuda.synchronize(dev)
     got = xs.cpu().view(torch.int16).numpy() if dtype == "bf16" else xs.cpu().numpy()
-    want = om.permute_rows(x.x, osp, 4)
+    want = om.permute_rows(x.x, osp, K)
     assert np.array_equal(got.view(want.dtype), want)
 
 
@@ -159,7 +163,7 @@ def test_moe_routing_workload_end_to_end(dev, num):
     osp, opp, ooff = om.sort_by_expert(oi, E)
     assert np.array_equal(sp, osp) and np.array_equal(pp, opp) and np.array_equal(off, ooff)
     xs = torch.empty((T * K, Hd), dtype=torch.bfloat16, device=dev)
-    pa.pa_moe_permute(xs, to_dev(x.x, dev), torch.from_numpy(sp).to(dev), K)
+    pa.pa_moe_permute(xs, to_dev(x.x, dev), torch.from_numpy(pp).to(dev), K)
     out = torch.empty((T, Hd), dtype=torch.bfloat16, device=dev)
     pa.pa_moe_combine(out, to_dev(x.y_sorted, dev), torch.from_numpy(w).to(dev), torch.from_numpy(pp).to(dev))
     torch.cuda.synchronize(dev)
