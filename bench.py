@@ -115,6 +115,16 @@ def traffic_for(num: int):
     return None if v is None else int(float(v))
 
 
+def moe_traffic_for(num: int):
+    """Calibrated HBM bytes per permute launch from the committed counter runs,
+    when they were taken on the current MoE kernel source; otherwise None."""
+    rec = read_traffic_file()
+    if rec.get("moe_kernel_source_sha256_16") != kernel_source_hash([os.path.join(CSRC, "pa_moe.hip")]):
+        return None
+    v = rec.get(f"moe_{num}_permute_traffic_bytes")
+    return None if v is None else int(float(v))
+
+
 def cpu_baseline(x, gpu_out, budget_s: float):
     """Time the fp64 oracle on host cores over a bounded sample of the workload:
     whole sequences in a fixed random order until the time budget is spent
@@ -511,8 +521,9 @@ def bench_moe(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
         "stage_us_mean": per_us,
         "algorithmic_bytes": nbytes,
         "tokens_per_s": round(T / (t * 1e-3), 1),
+        "kernel_source_sha256_16": kernel_source_hash([os.path.join(CSRC, "pa_moe.hip")]),
         "roofline": {"bound": "hbm", "achieved": round(pk, 2), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(pk / PEAK_GBS, 4), "traffic": None, "kernel": "pa_moe_permute",
+                     "frac": round(pk / PEAK_GBS, 4), "traffic": moe_traffic_for(num), "kernel": "pa_moe_permute",
                      "algorithmic_bytes_per_launch": int(nbytes["permute"])},
     }
     res["cpu_baseline"] = moe_cpu_baseline(x, cpu_budget) if cpu_budget > 0 else None
