@@ -115,13 +115,14 @@ def traffic_for(num: int):
     return None if v is None else int(float(v))
 
 
-def moe_traffic_for(num: int):
-    """Calibrated HBM bytes per permute launch from the committed counter runs,
-    when they were taken on the current MoE kernel source; otherwise None."""
+def moe_traffic_for(num: int, stage: str):
+    """Calibrated HBM bytes per launch of a MoE stage's kernel from the
+    committed counter runs, when they were taken on the current MoE kernel
+    source; otherwise None."""
     rec = read_traffic_file()
     if rec.get("moe_kernel_source_sha256_16") != kernel_source_hash([os.path.join(CSRC, "pa_moe.hip")]):
         return None
-    v = rec.get(f"moe_{num}_permute_traffic_bytes")
+    v = rec.get(f"moe_{num}_{stage}_traffic_bytes")
     return None if v is None else int(float(v))
 
 
@@ -508,7 +509,8 @@ def bench_moe(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
     t = float(ms.mean())
     total = sum(nbytes.values())
     gbs = total / (t * 1e-3) / 1e9
-    pk = nbytes["permute"] / (per_us["permute"] * 1e-6) / 1e9
+    dom = max(per_us, key=per_us.get)      # the dominant stage carries the roofline
+    pk = nbytes[dom] / (per_us[dom] * 1e-6) / 1e9
     res = {
         "metric": "MoE routing path (topk softmax, sort by expert, permute, combine) achieved HBM GB/s",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
@@ -523,8 +525,8 @@ def bench_moe(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
         "tokens_per_s": round(T / (t * 1e-3), 1),
         "kernel_source_sha256_16": kernel_source_hash([os.path.join(CSRC, "pa_moe.hip")]),
         "roofline": {"bound": "hbm", "achieved": round(pk, 2), "peak": PEAK_GBS, "unit": "GB/s",
-                     "frac": round(pk / PEAK_GBS, 4), "traffic": moe_traffic_for(num), "kernel": "pa_moe_permute",
-                     "algorithmic_bytes_per_launch": int(nbytes["permute"])},
+                     "frac": round(pk / PEAK_GBS, 4), "traffic": moe_traffic_for(num, dom), "kernel": "pa_moe_" + dom,
+                     "algorithmic_bytes_per_launch": int(nbytes[dom])},
     }
     res["cpu_baseline"] = moe_cpu_baseline(x, cpu_budget) if cpu_budget > 0 else None
     del scrub_buf

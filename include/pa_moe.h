@@ -65,7 +65,8 @@ int64_t pa_moe_sort_workspace_bytes(int32_t T, int32_t E, int32_t K);
  *   workspace       >= pa_moe_sort_workspace_bytes(T, E, K) bytes, 4-byte
  *                   aligned; its contents on entry do not matter.
  * Four launches (per-chunk ranks and counts, a scan over chunks per expert,
- * the expert offsets, the scatter). */
+ * the expert offsets, the scatter), or one single-workgroup launch for up to
+ * 4096 pairs; both give the same result. */
 int pa_moe_sort_by_expert(int32_t* sorted_pairs, int32_t* pair_pos, int32_t* expert_offsets,
                           const int32_t* topk_ids, int32_t T, int32_t E, int32_t K, void* workspace,
                           int64_t workspace_bytes, void* stream);

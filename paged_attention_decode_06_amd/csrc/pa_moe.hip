@@ -12,11 +12,12 @@
 //   * top-k softmax: one wave per token, E/64 logits per lane; max and sum by
 //     DPP reductions, then K rounds of (wave max of the untaken logits, the
 //     lowest id holding it by ballots).
-//   * sort: a stable counting sort in four launches. Chunks of 1024 pairs:
-//     every pair's rank among the earlier same-expert pairs of its chunk
-//     (wave ballots, then a prefix over the chunk's waves) and the chunk's
-//     per-expert counts; a scan over chunks per expert; the expert offsets;
-//     then every pair lands at offset + earlier chunks' count + rank.
+//   * sort: a stable counting sort. Chunks of 1024 pairs: every pair's rank
+//     among the earlier same-expert pairs of its chunk (wave ballots, then a
+//     prefix over the chunk's waves) and the chunk's per-expert counts; a
+//     scan over chunks per expert; the expert offsets; then every pair lands
+//     at offset + earlier chunks' count + rank. Four launches, or one
+//     workgroup walking the chunks in order for up to 8192 pairs.
 //   * permute and combine: one wave per row, 16-byte loads and stores; the
 //     combine gathers each token's K rows (no atomics) and sums them in fp32
 //     in the order j = 0..K-1.
@@ -40,17 +41,13 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? l
 #ifndef PA_MOE_NT
 #define PA_MOE_NT 1
 #endif
-// Rows read once and rows written once carry the non-temporal hint: with four
-// 1 KB slices per combine pass, measured 117.7 -> 104.4 us for the combine at
-// 16384 tokens x top 8 x 2048 bf16 (the permute measures the same with or
-// without it).
+// Rows read once carry the non-temporal hint: with four 1 KB slices per
+// combine pass, measured 117.7 -> 104.4 us for the combine at 16384 tokens x
+// top 8 x 2048 bf16. Stores stay plain: non-temporal stores made the
+// permute's scattered row writes slower (126 against 90 us, same workload).
 __device__ __forceinline__ u32x4 ld_rows(const void* p) {
   if constexpr (PA_MOE_NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return *reinterpret_cast<const u32x4*>(p);
-}
-__device__ __forceinline__ void st_rows(void* p, u32x4 v) {
-  if constexpr (PA_MOE_NT) __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
-  else *reinterpret_cast<u32x4*>(p) = v;
 }
 
 // ---------------------------------------------------------------- top-k softmax
@@ -152,11 +149,37 @@ __global__ __launch_bounds__(kThreads) void moe_topk_softmax_kernel(float* __res
 // ---------------------------------------------------------------- stable counting sort
 // Phase 1, one workgroup per chunk of 1024 pairs (16 waves of 64 consecutive
 // pairs): each wave ranks its pairs among the earlier same-expert pairs of the
-// wave (ballot per distinct expert: the leader's expert, the mask of lanes
-// holding it, the count of set bits below each lane) and counts them per
-// expert; a prefix over the 16 waves per expert turns that into the rank
-// within the chunk and the chunk's per-expert counts.
+// wave (the mask of lanes holding the same expert, the count of its set bits
+// below each lane) and counts them per expert; a prefix over the 16 waves per
+// expert turns that into the rank within the chunk and the chunk's per-expert
+// counts.
 constexpr int kSortWaves = kSortChunk / 64;
+static_assert(PA_MOE_MAX_EXPERTS <= 1024, "expert ids are matched on at most 10 bits");
+
+// Rank of each valid lane's expert e among the lower lanes of the wave that
+// hold the same expert; the lowest such lane stores the wave's count of e in
+// wcnt_row[e]. The lanes sharing e are found bit by bit: one ballot per bit
+// of the expert id (the bits of E - 1, at most 10), each lane keeping the
+// lanes that agree with it on that bit, so the cost does not depend on how
+// many distinct experts the wave holds.
+template <typename C>
+__device__ __forceinline__ int rank_in_wave(int e, bool valid, int lane, int ebits, C* wcnt_row) {
+  uint64_t m = __builtin_amdgcn_ballot_w64(valid);
+#pragma unroll
+  for (int b = 0; b < 10; ++b) {
+    if (b < ebits) {
+      const bool bit = ((e >> b) & 1) != 0;
+      const uint64_t mb = __builtin_amdgcn_ballot_w64(bit);
+      m &= bit ? mb : ~mb;
+    }
+  }
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  const int rw = __builtin_popcountll(m & below);
+  if (valid && rw == 0) wcnt_row[e] = (C)__builtin_popcountll(m);
+  return rw;
+}
+
+__device__ __forceinline__ int expert_bits(int E) { return E > 1 ? 32 - __builtin_clz((unsigned)(E - 1)) : 0; }
 
 __global__ __launch_bounds__(kSortChunk) void moe_sort_count_kernel(const int32_t* __restrict__ ids, int N, int E,
                                                                     int32_t* __restrict__ counts,
@@ -169,17 +192,7 @@ __global__ __launch_bounds__(kSortChunk) void moe_sort_count_kernel(const int32_
   const int e = valid ? clampi(ids[a], 0, E - 1) : -1;
   for (int i = t; i < kSortWaves * E; i += kSortChunk) wcnt[i] = 0;
   __syncthreads();
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  uint64_t todo = __builtin_amdgcn_ballot_w64(valid);
-  int rw = 0;
-  while (todo) {
-    const int leader = __builtin_ctzll(todo);
-    const int le = __builtin_amdgcn_readlane(e, leader);
-    const uint64_t m = __builtin_amdgcn_ballot_w64(e == le);
-    if (e == le) rw = __builtin_popcountll(m & below);
-    if (lane == leader) wcnt[w * E + le] = __builtin_popcountll(m);
-    todo &= ~m;
-  }
+  const int rw = rank_in_wave(e, valid, lane, expert_bits(E), wcnt + w * E);
   __syncthreads();
   if (t < E) {
     int run = 0;
@@ -258,6 +271,81 @@ __global__ __launch_bounds__(kSortChunk) void moe_sort_scatter_kernel(const int3
   }
 }
 
+// Small pair sets (up to kSortSmallChunks chunks), one workgroup, one launch:
+// the same per-chunk ranks, chunk after chunk, with each expert's running
+// count of the earlier chunks kept in LDS; then the offsets scan and the
+// scatter. Same result as the four-launch path.
+#ifndef PA_MOE_SORT_SMALL_CHUNKS
+#define PA_MOE_SORT_SMALL_CHUNKS 4
+#endif
+constexpr int kSortSmallChunks = PA_MOE_SORT_SMALL_CHUNKS;
+static_assert(kSortSmallChunks <= 8, "the single-workgroup sort is instantiated for up to 8 chunks");
+
+template <int R>
+__global__ __launch_bounds__(kSortChunk) void moe_sort_small_kernel(const int32_t* __restrict__ ids, int N, int E,
+                                                                    int32_t* __restrict__ sorted_pairs,
+                                                                    int32_t* __restrict__ pair_pos,
+                                                                    int32_t* __restrict__ offsets) {
+  static_assert(kSortChunk == PA_MOE_MAX_EXPERTS, "one thread per expert in the scans");
+  __shared__ uint16_t wcnt[kSortWaves * PA_MOE_MAX_EXPERTS];  // per-wave counts of one chunk (<= 64 each)
+  __shared__ int32_t run[PA_MOE_MAX_EXPERTS];                 // pairs of each expert in earlier chunks
+  __shared__ int32_t scan[PA_MOE_MAX_EXPERTS];
+  const int t = threadIdx.x, lane = t & 63, w = t >> 6;
+  int e[R], rk[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int a = r * kSortChunk + t;
+    e[r] = a < N ? clampi(ids[a], 0, E - 1) : -1;
+  }
+  run[t] = 0;
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    for (int i = t; i < kSortWaves * E; i += kSortChunk) wcnt[i] = 0;
+    __syncthreads();
+    const int rw = rank_in_wave(e[r], e[r] >= 0, lane, expert_bits(E), wcnt + w * E);
+    __syncthreads();
+    int chunk_total = 0;
+    if (t < E) {  // exclusive prefix over the chunk's waves, per expert
+#pragma unroll
+      for (int i = 0; i < kSortWaves; ++i) {
+        const int x = wcnt[i * E + t];
+        wcnt[i * E + t] = (uint16_t)chunk_total;
+        chunk_total += x;
+      }
+    }
+    __syncthreads();
+    rk[r] = e[r] >= 0 ? run[e[r]] + wcnt[w * E + e[r]] + rw : 0;
+    __syncthreads();
+    if (t < E) run[t] += chunk_total;
+  }
+  __syncthreads();
+  const int x = t < E ? run[t] : 0;
+  scan[t] = x;
+  __syncthreads();
+  for (int d = 1; d < PA_MOE_MAX_EXPERTS; d <<= 1) {
+    const int add = t >= d ? scan[t - d] : 0;
+    __syncthreads();
+    scan[t] += add;
+    __syncthreads();
+  }
+  const int off = scan[t] - x;
+  if (t < E) {
+    offsets[t] = off;
+    run[t] = off;
+  }
+  if (t == 0) offsets[E] = N;
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < R; ++r) {
+    const int a = r * kSortChunk + t;
+    if (a < N) {
+      const int pos = run[e[r]] + rk[r];
+      sorted_pairs[pos] = a;
+      pair_pos[a] = pos;
+    }
+  }
+}
+
 // ---------------------------------------------------------------- permute / combine
 // Token-major scatter: a wave reads token t's row once and writes it to the
 // K sorted positions of t's pairs. Every row of x is read from HBM once and
@@ -292,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void moe_permute_kernel(char* __restrict_
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int64_t off = off0 + (int64_t)u * 64 * 16;
-        if (off < row_bytes) st_rows(d + off, v[u]);
+        if (off < row_bytes) *reinterpret_cast<u32x4*>(d + off) = v[u];
       }
     }
   }
@@ -477,6 +565,15 @@ int pa_moe_sort_by_expert(int32_t* sorted_pairs, int32_t* pair_pos, int32_t* exp
     return PA_EALIGN;
   if (workspace_bytes < pa_moe_sort_workspace_bytes(T, E, K)) return PA_EINVAL;
   const int NC = (N + kSortChunk - 1) / kSortChunk;
+  if (NC <= kSortSmallChunks) {
+    (void)hipGetLastError();
+    const dim3 g(1), b(kSortChunk);
+    if (NC <= 1) hipLaunchKernelGGL(moe_sort_small_kernel<1>, g, b, 0, s, topk_ids, N, E, sorted_pairs, pair_pos, expert_offsets);
+    else if (NC <= 2) hipLaunchKernelGGL(moe_sort_small_kernel<2>, g, b, 0, s, topk_ids, N, E, sorted_pairs, pair_pos, expert_offsets);
+    else if (NC <= 4) hipLaunchKernelGGL(moe_sort_small_kernel<4>, g, b, 0, s, topk_ids, N, E, sorted_pairs, pair_pos, expert_offsets);
+    else hipLaunchKernelGGL(moe_sort_small_kernel<8>, g, b, 0, s, topk_ids, N, E, sorted_pairs, pair_pos, expert_offsets);
+    return finish() == hipSuccess ? PA_OK : PA_EHIP;
+  }
   int32_t* counts = reinterpret_cast<int32_t*>(workspace);
   int32_t* rank = counts + (int64_t)NC * E;
   int32_t* totals = rank + N;

@@ -84,8 +84,11 @@ def test_topk_ties_go_to_the_lower_id(dev):
 
 @pytest.mark.parametrize("T,E,K,dist", [(16384, 256, 8, "uniform"), (1, 256, 8, "uniform"), (100, 7, 3, "uniform"),
                                         (2000, 1024, 4, "uniform"), (3000, 256, 8, "one"), (777, 256, 8, "skew"),
-                                        (129, 16, 8, "uniform")])
+                                        (129, 16, 8, "uniform"), (512, 256, 8, "uniform"),
+                                        (4097, 64, 1, "uniform"), (500, 1024, 8, "skew"),
+                                        (1023, 1024, 8, "skew")])
 def test_sort_by_expert_exact(dev, T, E, K, dist):
+    """Both paths: one workgroup up to 4096 pairs (4 chunks), four launches above."""
     rng = np.random.default_rng(T * 7 + E)
     if dist == "uniform":
         ids = rng.integers(0, E, size=(T, K))
