@@ -64,6 +64,16 @@ __device__ __forceinline__ float rows_sum(float x) {
   return group_sum(x);
 }
 
+// gfx950 LDS transpose read of 16-bit data. Within each group of 16 lanes,
+// lane j reads 4 consecutive elements in[j][0..3] at its own address; lane i
+// receives out[i][e] = in[4e + i/4][i % 4]. So if lane j points at row
+// r0 + j/4, columns c0 + 4(j % 4) .. +3 of a row-major matrix, lane i gets
+// column c0 + i of rows r0 .. r0 + 3: the A operand layout of a 16x16 MFMA
+// (row = lane % 16, four consecutive k) read straight from row-major data.
+__device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(const_cast<void*>(p)));
+}
+
 struct PrefillParams {
   const void* q;
   const void* k;
@@ -120,6 +130,14 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     live[jj] = valid[jj] && pos >= 0;
     posc[jj] = live[jj] ? pos : kmax - 1;   // rows without keys compute a harmless stand-in
   }
+  // Smallest position among the wave's rows: key tiles that end at or below
+  // it need no causal mask (every row sees every key of the tile).
+  int min_pos = posc[0];
+#pragma unroll
+  for (int jj = 1; jj < NTW; ++jj) min_pos = min(min_pos, posc[jj]);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) min_pos = min(min_pos, __shfl_xor(min_pos, o));
+  const int wave_min_pos = __builtin_amdgcn_readfirstlane(min_pos);
   auto out_row = [&](int jj) -> T* {
     const int row = (w * NTW + jj) * 16 + g;
     return reinterpret_cast<T*>(P.out) + ((int64_t)(qb + tokr[jj]) * P.H + kvh * P.G + row % P.G) * D;
@@ -193,12 +211,16 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     issue_tile<T, D, TB, false>(tl, kbase, vbase, block_elems, phys, vb, g, grp);
   };
 
-  // The math of tile t: K as MFMA A operands (ka), V as raw rows (tl.v).
-  auto compute_ops = [&](tx8 (&ka)[TB][KK], BTile<D, TB>& tl, int t) {
+  // The math of tile t: K as MFMA A operands (ka); V as raw rows (tl.v,
+  // per-wave form) or as ready V^T A operands (vo, shared form).
+  static_assert(!SH || TB == 2, "the shared form takes two-block tiles");
+  auto compute_ops = [&](tx8 (&ka)[TB][KK], BTile<D, TB>& tl, const auto& vo, int t) {
     const int tok0 = t * TB * kBS;
+    const bool full = tok0 + TB * kBS - 1 <= wave_min_pos;  // no row of the wave needs the mask here
     // V rows at or past kmax (tail slots of the last block, blocks past the
-    // end) are zeroed: a zero weight times NaN would poison the sum.
-    if (tok0 + TB * kBS > kmax) {
+    // end) are zeroed: a zero weight times NaN would poison the sum. (The
+    // shared form zeroes them on their way into LDS.)
+    if (!SH && tok0 + TB * kBS > kmax) {
 #pragma unroll
       for (int b = 0; b < TB; ++b)
 #pragma unroll
@@ -219,15 +241,25 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
       }
       float x[TB][4];
       float mx = -INFINITY;
+      if (full) {
 #pragma unroll
-      for (int b = 0; b < TB; ++b)
+        for (int b = 0; b < TB; ++b)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int kp = tok0 + b * kBS + 4 * grp + i;
-          const float z = (kp <= posc[jj]) ? sc[b][i] * P.scale2 : -INFINITY;
-          x[b][i] = z;
-          mx = fmaxf(mx, z);
-        }
+          for (int i = 0; i < 4; ++i) {
+            x[b][i] = sc[b][i] * P.scale2;
+            mx = fmaxf(mx, x[b][i]);
+          }
+      } else {
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int kp = tok0 + b * kBS + 4 * grp + i;
+            const float z = (kp <= posc[jj]) ? sc[b][i] * P.scale2 : -INFINITY;
+            x[b][i] = z;
+            mx = fmaxf(mx, z);
+          }
+      }
       mx = rows_max(mx);
       const float mnew = fmaxf(m[jj], mx);  // finite: key 0 is in every row's first tile
       const float alpha = fast_exp2(m[jj] - mnew);
@@ -238,15 +270,25 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
       for (int b = 0; b < TB; ++b)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pb[b][i] = (T)fast_exp2(x[b][i] - mnew);
-          ps += (float)pb[b][i];
+          const float pe = fast_exp2(x[b][i] - mnew);
+          pb[b][i] = (T)pe;
+          ps += pe;
         }
       lsum[jj] = lsum[jj] * alpha + ps;
       if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
 #pragma unroll
         for (int a = 0; a < NACC; ++a) acc[jj][a] *= alpha;
       }
-      if constexpr (TB == 2) {
+      if constexpr (SH) {
+        tx8 pv;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          pv[i] = pb[0][i];
+          pv[4 + i] = pb[1][i];
+        }
+#pragma unroll
+        for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma32(vo[mt], pv, acc[jj][mt]);
+      } else if constexpr (TB == 2) {
         tx8 pv;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -315,20 +357,27 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
         const int c16 = 4 * kk + grp;
         ka[b][kk] = __builtin_bit_cast(tx8, ktile[(b * 16 + g) * KCH + (c16 ^ g)]);
       }
-    compute_ops(ka, tl, t);
+    const tx8 vo_unused[NACC] = {};  // the per-wave form takes V from tl
+    compute_ops(ka, tl, vo_unused, t);
   };
 
   if constexpr (SH) {
     // Shared path: the workgroup loads each K/V tile once, 16 bytes per
-    // thread-chunk, into one of two LDS stages (K XOR-swizzled by row as
-    // above, V row-major); every wave reads its MFMA operands from there.
-    // The next tile's chunks are in registers while this tile's math runs;
-    // one barrier per tile publishes the next stage.
+    // thread-chunk, into one of two LDS stages; every wave reads its MFMA
+    // operands there. Rows are padded to KCH + 1 chunks, so the K operand
+    // reads (row g, chunk 4kk + grp) and the V transpose reads (rows
+    // 4grp + g/4, two 8-byte halves) spread over all banks, and every
+    // operand address is the lane's base plus a constant. V rows at or past
+    // kmax go in as zeros. The next tile's chunks are in registers while this
+    // tile's math runs; one barrier per tile publishes the next stage.
     constexpr int TCH = TB * 16 * KCH;               // 16-byte chunks of K (or V) per tile
     constexpr int PER = 2 * TCH / (NW * 64);         // chunks per thread per tile
     static_assert(PER * NW * 64 == 2 * TCH, "tile chunks must split evenly over the threads");
-    u32x4* kst = reinterpret_cast<u32x4*>(smem);     // [2][TCH]
-    u32x4* vst = kst + 2 * TCH;                      // [2][TCH]
+    static_assert(SHD % 2 == 0, "stage parity follows the slot index");
+    constexpr int RS = KCH + 1;                      // padded row stride (chunks)
+    constexpr int STG = TB * 16 * RS;                // chunks per stage
+    u32x4* kst = reinterpret_cast<u32x4*>(smem);     // [2][TB*16][RS]
+    u32x4* vst = kst + 2 * STG;                      // [2][TB*16][RS]
     auto fetch = [&](u32x4 (&stage)[PER], int t) {
       if (t % CH == 0) refill(t / CH);
       int64_t phys[TB];
@@ -351,6 +400,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
             pb = phys[bb];
             ok = vb[bb];
           }
+        if (kv && (t * TB + b) * kBS + row >= kmax) ok = false;
         const T* src = (kv ? vbase : kbase) + pb * block_elems + row * D + c * 8;
         stage[u] = ok ? ld16(src) : (u32x4){0u, 0u, 0u, 0u};
       }
@@ -361,18 +411,18 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
         const int id = u * NW * 64 + (int)threadIdx.x;
         const int kv = id / TCH, r = id % TCH;
         const int b = r / (16 * KCH), row = (r / KCH) % 16, c = r % KCH;
-        if (kv == 0)
-          kst[buf * TCH + (b * 16 + row) * KCH + (c ^ row)] = stage[u];
-        else
-          vst[buf * TCH + (b * 16 + row) * KCH + c] = stage[u];
+        (kv ? vst : kst)[buf * STG + (b * 16 + row) * RS + c] = stage[u];
       }
     };
+    const u32x4* klane = kst + g * RS + grp;                               // + b*16*RS + 4kk
+    const char* vlane = reinterpret_cast<const char*>(vst) +
+                        ((4 * grp + (g >> 2)) * RS + ((g >> 1) & 1)) * 16 + (g & 1) * 8;  // + 32 mt
     // SHD register stages: tile t's slot is t % SHD. At the top of iteration
     // t that slot is free (tile t went to LDS in iteration t - 1) and takes
     // the loads of tile t + SHD, which then have SHD tiles of math to arrive
     // in; after the math, tile t + 1 goes from its slot to the other LDS
-    // stage. The loop runs in groups of SHD so every slot index is a
-    // compile-time constant.
+    // stage. The loop runs in groups of SHD so every slot index and stage
+    // parity is a compile-time constant.
     u32x4 stage[SHD][PER];
 #pragma unroll
     for (int d = 0; d < SHD; ++d)
@@ -385,23 +435,26 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     for (int d = 0; d < SHD; ++d) {
       const int t = t0 + d;
       if (t >= ntiles) break;
-      const int buf = t & 1;
+      const int buf = d & 1;  // == t & 1: t0 is a multiple of SHD
       // slot d held tile t, already in LDS: refill it with tile t + SHD
       if (t + SHD < ntiles) fetch(stage[d], t + SHD);
       tx8 ka[TB][KK];
 #pragma unroll
-      for (int b = 0; b < TB; ++b) {
+      for (int b = 0; b < TB; ++b)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const int c16 = 4 * kk + grp;
-          ka[b][kk] = __builtin_bit_cast(tx8, kst[buf * TCH + (b * 16 + g) * KCH + (c16 ^ g)]);
-        }
+        for (int kk = 0; kk < KK; ++kk)
+          ka[b][kk] = __builtin_bit_cast(tx8, klane[buf * STG + b * 16 * RS + 4 * kk]);
+      // V^T operand of M-tile mt (head dims 16mt .. 16mt+15): keys
+      // 4grp .. 4grp+3 from block 0 and the same from block 1, in the order
+      // the QK accumulator hands P over.
+      tx8 vo[NACC];
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-          for (int h = 0; h < NH; ++h) tl.v[b][rr][h] = vst[buf * TCH + (b * 16 + 4 * grp + rr) * KCH + 16 * h + g];
+      for (int mt = 0; mt < NACC; ++mt) {
+        const i16x4 lo = lds_read_tr16(vlane + (buf * STG) * 16 + 32 * mt);
+        const i16x4 hi = lds_read_tr16(vlane + (buf * STG + 16 * RS) * 16 + 32 * mt);
+        vo[mt] = __builtin_bit_cast(tx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-      compute_ops(ka, tl, t);
+      compute_ops(ka, tl, vo, t);
       if (t + 1 < ntiles) deposit(stage[(d + 1) % SHD], buf ^ 1);
       __syncthreads();
     }
@@ -416,14 +469,20 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     }
   }
 
-  // acc[jj][h*8 + j][i] holds dim 128h + 32*grp + 8i + j of the lane's row:
-  // for fixed (h, i) the 8 values j = 0..7 are consecutive dims.
+  // Per-wave form: acc[jj][h*8 + j][i] holds dim 128h + 32*grp + 8i + j of
+  // the lane's row (for fixed (h, i) the 8 values j = 0..7 are consecutive
+  // dims). Shared form: acc[jj][mt][i] holds dim 16mt + 4grp + i.
 #pragma unroll
   for (int jj = 0; jj < NTW; ++jj) {
     const float tot = rows_sum(lsum[jj]);
     if (!valid[jj]) continue;
     const float inv = live[jj] ? 1.f / tot : 0.f;
     T* orow = out_row(jj);
+    if constexpr (SH) {  // acc[jj][mt][i] holds dim 16mt + 4grp + i
+#pragma unroll
+      for (int mt = 0; mt < NACC; ++mt) store4<T>(orow, 16 * mt + 4 * grp, acc[jj][mt] * inv);
+      continue;
+    }
 #pragma unroll
     for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -458,13 +517,13 @@ hipError_t launch_prefill_t(PrefillParams P, int D, int maxq, const Launch& L) {
     if (tiles(128) <= kPrefillSmallGrid) {
       constexpr int NW = 8, NTW = 1, TB = 2;
       P.QT = 128 / P.G;
-      const size_t smem = (size_t)4 * TB * 16 * 128 * sizeof(T);  // two stages of K and V
+      const size_t smem = (size_t)4 * TB * 16 * (128 / 8 + 1) * 16;  // two stages of K and V, padded rows
       return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true, 4>, dim3((unsigned)tiles(128)), dim3(NW * 64), smem,
                     L, P);
     }
     constexpr int NW = 8, NTW = 2, TB = 2;
     P.QT = 256 / P.G;
-    const size_t smem = (size_t)4 * TB * 16 * 128 * sizeof(T);
+    const size_t smem = (size_t)4 * TB * 16 * (128 / 8 + 1) * 16;
     return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true, 2>, dim3((unsigned)tiles(256)), dim3(NW * 64), smem, L,
                   P);
   }
