@@ -364,20 +364,23 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   if constexpr (SH) {
     // Shared path: the workgroup loads each K/V tile once, 16 bytes per
     // thread-chunk, into one of two LDS stages; every wave reads its MFMA
-    // operands there. Rows are padded to KCH + 1 chunks, so the K operand
-    // reads (row g, chunk 4kk + grp) and the V transpose reads (rows
-    // 4grp + g/4, two 8-byte halves) spread over all banks, and every
-    // operand address is the lane's base plus a constant. V rows at or past
-    // kmax go in as zeros. The next tile's chunks are in registers while this
+    // operands there. K rows are XOR-swizzled (chunk c of row r at c ^ r,
+    // as in the per-wave tile); V rows are padded by two 16-byte chunks, so
+    // the four rows a transpose read takes per 16 lanes (8 dwords each) start
+    // 8 dwords apart. Both read patterns measured free of bank conflicts
+    // (padded K rows were not: 17- and 18-chunk strides conflicted on three
+    // in four LDS cycles of the K reads). V rows at or past kmax go in as
+    // zeros. The next tile's chunks are in registers while this
     // tile's math runs; one barrier per tile publishes the next stage.
     constexpr int TCH = TB * 16 * KCH;               // 16-byte chunks of K (or V) per tile
     constexpr int PER = 2 * TCH / (NW * 64);         // chunks per thread per tile
     static_assert(PER * NW * 64 == 2 * TCH, "tile chunks must split evenly over the threads");
     static_assert(SHD % 2 == 0, "stage parity follows the slot index");
-    constexpr int RS = KCH + 1;                      // padded row stride (chunks)
-    constexpr int STG = TB * 16 * RS;                // chunks per stage
-    u32x4* kst = reinterpret_cast<u32x4*>(smem);     // [2][TB*16][RS]
-    u32x4* vst = kst + 2 * STG;                      // [2][TB*16][RS]
+    static_assert(KCH == 16, "the K swizzle spans the 16 chunks of a 128-dim row");
+    constexpr int RSV = KCH + 2;                     // padded V row stride (chunks)
+    constexpr int STGK = TB * 16 * KCH, STGV = TB * 16 * RSV;  // chunks per stage
+    u32x4* kst = reinterpret_cast<u32x4*>(smem);     // [2][TB*16][KCH]
+    u32x4* vst = kst + 2 * STGK;                     // [2][TB*16][RSV]
     auto fetch = [&](u32x4 (&stage)[PER], int t) {
       if (t % CH == 0) refill(t / CH);
       int64_t phys[TB];
@@ -411,12 +414,17 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
         const int id = u * NW * 64 + (int)threadIdx.x;
         const int kv = id / TCH, r = id % TCH;
         const int b = r / (16 * KCH), row = (r / KCH) % 16, c = r % KCH;
-        (kv ? vst : kst)[buf * STG + (b * 16 + row) * RS + c] = stage[u];
+        if (kv)
+          vst[buf * STGV + (b * 16 + row) * RSV + c] = stage[u];
+        else
+          kst[buf * STGK + (b * 16 + row) * KCH + (c ^ row)] = stage[u];
       }
     };
-    const u32x4* klane = kst + g * RS + grp;                               // + b*16*RS + 4kk
+    const u32x4* klane[KK];                                                // + b*16*KCH
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) klane[kk] = kst + g * KCH + ((4 * kk + grp) ^ g);
     const char* vlane = reinterpret_cast<const char*>(vst) +
-                        ((4 * grp + (g >> 2)) * RS + ((g >> 1) & 1)) * 16 + (g & 1) * 8;  // + 32 mt
+                        ((4 * grp + (g >> 2)) * RSV + ((g >> 1) & 1)) * 16 + (g & 1) * 8;  // + 32 mt
     // SHD register stages: tile t's slot is t % SHD. At the top of iteration
     // t that slot is free (tile t went to LDS in iteration t - 1) and takes
     // the loads of tile t + SHD, which then have SHD tiles of math to arrive
@@ -443,15 +451,15 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
       for (int b = 0; b < TB; ++b)
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk)
-          ka[b][kk] = __builtin_bit_cast(tx8, klane[buf * STG + b * 16 * RS + 4 * kk]);
+          ka[b][kk] = __builtin_bit_cast(tx8, klane[kk][buf * STGK + b * 16 * KCH]);
       // V^T operand of M-tile mt (head dims 16mt .. 16mt+15): keys
       // 4grp .. 4grp+3 from block 0 and the same from block 1, in the order
       // the QK accumulator hands P over.
       tx8 vo[NACC];
 #pragma unroll
       for (int mt = 0; mt < NACC; ++mt) {
-        const i16x4 lo = lds_read_tr16(vlane + (buf * STG) * 16 + 32 * mt);
-        const i16x4 hi = lds_read_tr16(vlane + (buf * STG + 16 * RS) * 16 + 32 * mt);
+        const i16x4 lo = lds_read_tr16(vlane + (buf * STGV) * 16 + 32 * mt);
+        const i16x4 hi = lds_read_tr16(vlane + (buf * STGV + 16 * RSV) * 16 + 32 * mt);
         vo[mt] = __builtin_bit_cast(tx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
       compute_ops(ka, tl, vo, t);
@@ -517,13 +525,13 @@ hipError_t launch_prefill_t(PrefillParams P, int D, int maxq, const Launch& L) {
     if (tiles(128) <= kPrefillSmallGrid) {
       constexpr int NW = 8, NTW = 1, TB = 2;
       P.QT = 128 / P.G;
-      const size_t smem = (size_t)4 * TB * 16 * (128 / 8 + 1) * 16;  // two stages of K and V, padded rows
+      const size_t smem = (size_t)2 * TB * 16 * (2 * (128 / 8) + 2) * 16;  // two stages of K and (padded) V
       return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true, 4>, dim3((unsigned)tiles(128)), dim3(NW * 64), smem,
                     L, P);
     }
     constexpr int NW = 8, NTW = 2, TB = 2;
     P.QT = 256 / P.G;
-    const size_t smem = (size_t)4 * TB * 16 * (128 / 8 + 1) * 16;
+    const size_t smem = (size_t)2 * TB * 16 * (2 * (128 / 8) + 2) * 16;
     return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true, 2>, dim3((unsigned)tiles(256)), dim3(NW * 64), smem, L,
                   P);
   }
