@@ -58,7 +58,7 @@ def sort(ids, E, dev):
 
 
 @pytest.mark.parametrize("T,E,K", [(1000, 256, 8), (37, 64, 1), (300, 100, 8), (64, 1024, 32), (5, 8, 8),
-                                   (129, 256, 2)])
+                                   (129, 256, 2), (4096, 256, 8), (5001, 100, 16), (4099, 8, 3), (6000, 256, 17)])
 @pytest.mark.parametrize("renorm", [False, True])
 def test_topk_softmax(dev, T, E, K, renorm):
     rng = np.random.default_rng(T + E + K)
@@ -70,9 +70,10 @@ def test_topk_softmax(dev, T, E, K, renorm):
     assert np.abs(w - ow).max() <= 2e-6
 
 
-def test_topk_ties_go_to_the_lower_id(dev):
+@pytest.mark.parametrize("T", [500, 4100])   # one wave per token / 16 lanes per token
+def test_topk_ties_go_to_the_lower_id(dev, T):
     rng = np.random.default_rng(1)
-    lg = (np.round(rng.standard_normal((500, 256)) * 2) / 2).astype(np.float32)   # many exact ties
+    lg = (np.round(rng.standard_normal((T, 256)) * 2) / 2).astype(np.float32)   # many exact ties
     lg[0, :] = 1.5                                                                   # all tied
     say("topk with ties")
     w, i = topk(lg, 8, True, dev)
