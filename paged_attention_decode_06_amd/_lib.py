@@ -85,6 +85,16 @@ def header_functions(paths=None) -> list[str]:
     return sorted(names)
 
 
+def _hip_runtimes() -> list[str]:
+    """Paths of the HIP runtime libraries mapped into this process (Linux)."""
+    try:
+        with open("/proc/self/maps") as f:
+            paths = {line.split()[-1] for line in f if "libamdhip64" in line}
+    except OSError:
+        return []
+    return sorted({os.path.realpath(x) for x in paths})
+
+
 def load(path: str | None = None) -> ctypes.CDLL:
     """Load the HIP library (once). Raises if it has not been built."""
     global _lib
@@ -95,7 +105,16 @@ def load(path: str | None = None) -> ctypes.CDLL:
         raise RuntimeError(f"{p} is missing: build it first with "
                            "`python -c 'import __graft_entry__ as g; g.build()'` "
                            "or `python -m paged_attention_decode_06_amd._build`")
+    # torch ships its own HIP runtime. Loaded first, it is the one the library
+    # binds to; loaded after the library, the process would map two runtimes,
+    # and torch's streams and allocations would be handed to the other one
+    # (every launch then fails).
+    import torch  # noqa: F401
     lib = ctypes.CDLL(p)
+    runtimes = _hip_runtimes()
+    if len(runtimes) > 1:
+        raise RuntimeError("more than one HIP runtime is mapped in this process "
+                           f"({', '.join(runtimes)}): import torch before loading {p}")
     for name, (res, args) in _SIGS.items():
         fn = getattr(lib, name)
         fn.restype, fn.argtypes = res, args

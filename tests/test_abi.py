@@ -215,3 +215,18 @@ def test_moe_validation(lib):
     assert lib.pa_moe_combine(a, a, a, a, 10, 40, 2048, L.PA_BF16, n) == L.PA_EUNSUPPORTED
     assert lib.pa_moe_combine(n, n, n, n, 0, 8, 2048, L.PA_F32, n) == L.PA_OK
     assert f is not None
+
+
+def test_load_binds_to_one_hip_runtime():
+    """Loading the library before torch must still leave one HIP runtime in
+    the process (two runtimes make every launch on torch's streams fail)."""
+    import os
+    import subprocess
+    import sys
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    code = ("from paged_attention_decode_06_amd import _lib as L\n"
+            "L.load()\n"
+            "print(len(L._hip_runtimes()))\n")
+    res = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stderr
+    assert res.stdout.strip().splitlines()[-1] == "1"
