@@ -41,6 +41,7 @@ constexpr int kPart = PA_PARTITION_SIZE;
 constexpr int kThresh = PA_V2_THRESHOLD;
 constexpr int kReduceThreads = 256;
 constexpr int kReduceChunk = 32;   // head dims per reduce workgroup
+constexpr int kCompactMaxSeqs = 1024;  // largest batch mapped through the compact work list
 
 struct Params {
   const void* q;
@@ -57,6 +58,7 @@ struct Params {
   int64_t NB;
   int S, H, Hkv, G, MB, Pmax, mode;
   int PS;        // tokens per partition (512, or the opt-in 256)
+  int compact;   // workgroups follow the compact work list (item_of)
   float scale2;  // softmax scale times log2(e): logits are kept in base-2 units
 };
 
@@ -90,6 +92,84 @@ __device__ __forceinline__ int work_range(const Params& P, int s, int p, Range& 
   r.blk_begin = r.tok_begin / kBS;
   r.blk_end = (r.tok_end + kBS - 1) / kBS;
   return 1;
+}
+
+// Work item of workgroup b in the compact order, computed by every wave from
+// seq_lens alone: first one item per KV head for every sequence that takes a
+// single pass (a zero-length context included: it writes zeros), in sequence
+// order; then, sequence by sequence, the partitions of every partitioned
+// sequence as (partition, KV head) pairs. Workgroups past the last item
+// return false. The host sizes the grid for the longest table, so the unused
+// workgroups trail the used ones instead of sitting between them: on a batch
+// of mixed lengths the interleaved empty workgroups cost up to a third of the
+// kernel time, and the long single-pass items go first so that they do not
+// finish last.
+__device__ __forceinline__ int clamp_len(const Params& P, int s) {
+  int L = P.sl[s];
+  const int cap = P.MB * kBS;
+  L = L > cap ? cap : L;
+  return L < 0 ? 0 : L;
+}
+
+__device__ __forceinline__ bool item_of(const Params& P, int b, int lane, int& s_out, int& kvh_out,
+                                        int& p_out) {
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes < this one
+  // Pass 1: number of single-pass sequences (AUTO mode; V2 mode has none).
+  int n1 = 0;
+  if (P.mode == PA_MODE_AUTO) {
+    for (int c = 0; c < P.S; c += 64) {
+      const int s = c + lane;
+      const bool one = s < P.S && clamp_len(P, s) <= kThresh;
+      n1 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(one));
+    }
+  }
+  const int total1 = n1 * P.Hkv;
+  if (b < total1) {
+    int r = b / P.Hkv;  // rank of the sequence among the single-pass ones
+    for (int c = 0; c < P.S; c += 64) {
+      const int s = c + lane;
+      const bool one = s < P.S && clamp_len(P, s) <= kThresh;
+      const uint64_t mask = __builtin_amdgcn_ballot_w64(one);
+      const int cnt = __builtin_popcountll(mask);
+      if (r < cnt) {
+        const bool hit = one && __builtin_popcountll(mask & below) == r;
+        s_out = __builtin_amdgcn_readfirstlane(c + __builtin_ctzll(__builtin_amdgcn_ballot_w64(hit)));
+        kvh_out = b % P.Hkv;
+        p_out = 0;
+        return true;
+      }
+      r -= cnt;
+    }
+    return false;
+  }
+  // Pass 2: partitioned sequences, Hkv * ceil(L / PS) items each.
+  int r = b - total1;
+  for (int c = 0; c < P.S; c += 64) {
+    const int s = c + lane;
+    int n = 0;
+    if (s < P.S) {
+      const int L = clamp_len(P, s);
+      if (P.mode == PA_MODE_V2 || L > kThresh) n = (L + P.PS - 1) / P.PS * P.Hkv;
+    }
+    int incl = n;  // inclusive prefix sum over the chunk's lanes
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const int y = __shfl_up(incl, o);
+      if (lane >= o) incl += y;
+    }
+    const int tot = __shfl(incl, 63);
+    if (r < tot) {
+      const bool hit = n > 0 && r >= incl - n && r < incl;
+      const int l = __builtin_ctzll(__builtin_amdgcn_ballot_w64(hit));
+      const int local = __builtin_amdgcn_readfirstlane(r - (__shfl(incl, l) - __shfl(n, l)));
+      s_out = c + l;
+      p_out = local / P.Hkv;
+      kvh_out = local % P.Hkv;
+      return true;
+    }
+    r -= tot;
+  }
+  return false;
 }
 
 // Physical block id of logical block `blk` (wave-uniform), range-checked.
@@ -265,10 +345,12 @@ void pa_partition_h16(Params P) {
 
   // Workgroup b serves (pair b % pairs, partition b / pairs): its NW waves
   // take the item's tiles t0, t0 + dt, ... and merge through LDS at the end.
+  // (compact grids map workgroups through item_of instead).
   const int pairs = P.S * P.Hkv;
-  const int pair = blockIdx.x % pairs, p = blockIdx.x / pairs;
+  int pair = blockIdx.x % pairs, p = blockIdx.x / pairs;
   const int t0 = w, dt = NW;
-  const int s = pair / P.Hkv, kvh = pair % P.Hkv;
+  int s = pair / P.Hkv, kvh = pair % P.Hkv;
+  if (P.compact && !item_of(P, blockIdx.x, lane, s, kvh, p)) return;
   const int32_t* bt_row = P.bt + (int64_t)s * P.MB;
   // The first block-id list, read speculatively (a single pass starts at block
   // 0, partition p at block 32p; a workgroup with nothing to do drops it).
@@ -513,8 +595,9 @@ __global__ __launch_bounds__(NW * 64) void pa_partition_f32(Params P) {
   const int g = lane & 15, grp = lane >> 4;
 
   const int pairs = P.S * P.Hkv;
-  const int pair = blockIdx.x % pairs, p = blockIdx.x / pairs;
-  const int s = pair / P.Hkv, kvh = pair % P.Hkv;
+  int pair = blockIdx.x % pairs, p = blockIdx.x / pairs;
+  int s = pair / P.Hkv, kvh = pair % P.Hkv;
+  if (P.compact && !item_of(P, blockIdx.x, lane, s, kvh, p)) return;
   Range r;
   const int what = work_range(P, s, p, r);
   if (what == 0) return;
@@ -912,6 +995,10 @@ Params make_params(void* out, const void* q, const void* k, const void* v, const
   P.S = sh->num_seqs; P.H = sh->num_heads; P.Hkv = sh->num_kv_heads;
   P.G = sh->num_heads / sh->num_kv_heads; P.MB = sh->max_blocks_per_seq;
   P.Pmax = (int)max_partitions(sh); P.mode = mode; P.PS = partition_size(sh);
+  // One sequence, or single-pass only: the direct (partition, sequence, KV
+  // head) order is already compact. Very large batches keep it too: every
+  // workgroup of a compact grid scans all sequence lengths.
+  P.compact = mode != PA_MODE_V1 && P.S > 1 && P.S <= kCompactMaxSeqs && P.Pmax > 1;
   P.scale2 = scale * kLog2e;
   return P;
 }
