@@ -188,6 +188,52 @@ def test_zero_length_contexts_write_zeros(dev, mode):
     assert_close(x, out, seqs=[1, 3], label=mode)
 
 
+@pytest.mark.parametrize("mode", MODES)
+def test_compact_work_list_over_several_chunks(dev, mode):
+    """130 sequences: the kernel's work-list scan walks three 64-sequence
+    chunks (the last one partial). Zero, short, threshold-edge and long
+    contexts are mixed; every output row is checked, and on the partitioned
+    path every partial of every sequence with partitions."""
+    rng = np.random.default_rng(1130)
+    lens = rng.integers(1, 3000, size=130)
+    lens[::7] = 0
+    lens[5::11] = rng.integers(8193, 20000, size=lens[5::11].size)
+    lens[3], lens[4], lens[127] = 8192, 8193, 20000
+    cfg = W.DecodeConfig("compact130", lens.size, 16, 2, 128, "bf16", ("custom",))
+    x = W.make_inputs(cfg, seed=1130, seq_lens=lens.tolist())
+    say(f"compact work list: 130 seqs, mode={mode}")
+    out, (es, ml, to) = run(x, dev, mode)
+    got = assert_close(x, out, label=f"compact {mode}")
+    for s_ in np.where(lens == 0)[0]:
+        assert np.array_equal(got[s_], np.zeros_like(got[s_]))
+    if mode == "v1":
+        return
+    lists = oracle.gather_list(x.block_tables, x.seq_lens)
+    es, ml, to = es.cpu().numpy(), ml.cpu().numpy(), to.cpu().numpy()
+    for s_, L in enumerate(lens.tolist()):
+        P = 0 if (mode == "auto" and L <= 8192) else oracle.num_partitions(L, 512)
+        if P:
+            m, l, o = oracle.partition_stats(x.q[s_], x.k_cache, x.v_cache, lists[s_], L, x.scale, "bf16", 512)
+            assert np.abs(ml[s_, :, :P] - m).max() <= 1e-3
+            assert (np.abs(es[s_, :, :P] - l) / l).max() <= 1e-2
+            assert max_err(to[s_, :, :P], o) <= 2e-2
+        assert np.isnan(ml[s_, :, P:]).all() and np.isnan(to[s_, :, P:]).all()   # untouched
+
+
+def test_batch_above_the_work_list_limit(dev):
+    """1100 sequences (above the batch size the compact work list serves):
+    the grid keeps its direct order; mostly short contexts with a long
+    partitioned one every 100 sequences, every row checked."""
+    rng = np.random.default_rng(1100)
+    lens = rng.integers(0, 65, size=1100)
+    lens[50::100] = rng.integers(9000, 12001, size=lens[50::100].size)
+    cfg = W.DecodeConfig("direct1100", lens.size, 16, 2, 128, "bf16", ("custom",))
+    x = W.make_inputs(cfg, seed=1100, seq_lens=lens.tolist())
+    say("direct order: 1100 seqs")
+    out, _ = run(x, dev, "auto")
+    assert_close(x, out, label="direct 1100")
+
+
 def test_empty_batch(dev):
     cfg = W.DecodeConfig("empty", 0, 16, 2, 128, "bf16", ("custom",))
     x = W.make_inputs(cfg, seed=1, seq_lens=np.zeros(0, np.int32))
