@@ -234,6 +234,44 @@ def test_batch_above_the_work_list_limit(dev):
     assert_close(x, out, label="direct 1100")
 
 
+def test_graph_replay_matches_eager(dev):
+    """pa_decode captured in a HIP graph (as a serving loop would capture a
+    decode step): each replay, with q changed in place and eager work in
+    between, matches an eager call on the same inputs bit for bit, and the
+    last one matches the oracle."""
+    lens = [37, 9000, 513, 0, 20000, 8192]
+    x = W.make_inputs(W.DECODE_WORKLOADS[2], seed=91, seq_lens=lens)
+    d = W.to_device(x, dev)
+    q, kc, vc, bt, sl = d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens"]
+    sh = pa.make_shape(q, kc, bt)
+    es, ml, to = pa.alloc_partials(sh, dev)
+    out = torch.empty_like(q)
+    side = torch.cuda.Stream(dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(side):
+        pa.pa_decode(out, q, kc, vc, bt, sl, x.scale, es, ml, to)
+    torch.cuda.current_stream(dev).wait_stream(side)
+    torch.cuda.synchronize(dev)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        pa.pa_decode(out, q, kc, vc, bt, sl, x.scale, es, ml, to)
+    torch.cuda.synchronize(dev)
+    say("graph replay vs eager")
+    gen = torch.Generator(device="cpu").manual_seed(92)
+    ref_out = torch.empty_like(q)
+    es2, ml2, to2 = pa.alloc_partials(sh, dev)
+    for rep in range(3):
+        q.copy_(torch.randn(q.shape, generator=gen).to(q.dtype))
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize(dev)
+        pa.pa_decode(ref_out, q, kc, vc, bt, sl, x.scale, es2, ml2, to2)
+        torch.cuda.synchronize(dev)
+        assert torch.equal(out, ref_out), f"replay {rep}"
+    x.q[...] = q.cpu().view(torch.int16).numpy().view(np.uint16)   # bf16 bits, as the workload stores q
+    assert_close(x, out, label="graph replay")
+
+
 def test_empty_batch(dev):
     cfg = W.DecodeConfig("empty", 0, 16, 2, 128, "bf16", ("custom",))
     x = W.make_inputs(cfg, seed=1, seq_lens=np.zeros(0, np.int32))
