@@ -703,9 +703,9 @@ __global__ __launch_bounds__(NW * 64) void pa_partition_f32(Params P) {
 // Phase 2 (project_6 commit cd0d9e1a, "V2 implementation", phase 2): one
 // workgroup per (sequence, head, CW-wide slice of the head dims). Thread t
 // owns float4 t % (CW/4) of the slice and partitions t / (CW/4) + PG*u of
-// each group of PG*NU partitions; all loads of a group are issued at once,
-// then a block-wide max, then the weighted sum. Groups beyond the first
-// rescale the running sums to the new max. The host picks CW: full rows (one
+// each group of PG*NU partitions; all loads of a group are issued at once
+// and folded into the thread's running (max, weight sum, output), rescaled
+// when its max grows; one LDS exchange then merges the per-thread triples. The host picks CW: full rows (one
 // coalesced 1 KB row per wave at D = 256) when there are enough (sequence,
 // head) rows to fill the GPU, narrow slices (more workgroups) otherwise.
 // With SPEC (small partial sets, where the kernel is latency-bound) the first
@@ -726,13 +726,13 @@ __global__ __launch_bounds__(kReduceThreads) void pa_lse_reduce_kernel(ReducePar
   constexpr int F4 = CW / 4;                 // float4 per slice
   constexpr int PG = kReduceThreads / F4;    // partition groups
   constexpr int NU = 16;                     // partitions per thread per group
-  __shared__ float red[kReduceThreads / 64];
+  __shared__ float sm_m[PG], sm_c[PG];
   __shared__ f32x4 part[kReduceThreads];
   const int nchunk = R.D / CW;
   const int dc = blockIdx.x % nchunk;
   const int sh = blockIdx.x / nchunk;
   const int s = sh / R.H;
-  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int t = threadIdx.x;
   const float* ml = R.max_logits + (int64_t)sh * R.Pmax;
   const float* es = R.exp_sums + (int64_t)sh * R.Pmax;
   const float* to = R.tmp_out + (int64_t)sh * R.Pmax * R.D + dc * CW;
@@ -761,6 +761,10 @@ __global__ __launch_bounds__(kReduceThreads) void pa_lse_reduce_kernel(ReducePar
   if (R.mode == PA_MODE_AUTO && L <= kThresh) return;
   const int np = (L + R.PS - 1) / R.PS;
 
+  // Each thread keeps a running (max, weight sum, weighted output) over its
+  // own partitions, rescaled when its max grows; the workgroup then merges
+  // the PG per-group triples once, through LDS (threads of one group hold the
+  // same partitions, so their maxima and sums agree).
   float M = -INFINITY, ctot = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int base = 0; base < np; base += PG * NU) {
@@ -779,38 +783,39 @@ __global__ __launch_bounds__(kReduceThreads) void pa_lse_reduce_kernel(ReducePar
     float cm = mv[0];
 #pragma unroll
     for (int u = 1; u < NU; ++u) cm = fmaxf(cm, mv[u]);
+    const float Mn = fmaxf(M, cm);
+    if (Mn > -INFINITY) {
+      const float a = (M > -INFINITY) ? fast_exp2((M - Mn) * kLog2e) : 0.f;
+      acc *= a;
+      ctot *= a;
+      M = Mn;
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) cm = fmaxf(cm, __shfl_xor(cm, o));
-    if (lane == 0) red[wv] = cm;
-    __syncthreads();
-    float Mc = red[0];
-#pragma unroll
-    for (int i = 1; i < kReduceThreads / 64; ++i) Mc = fmaxf(Mc, red[i]);
-    __syncthreads();
-    const float Mn = fmaxf(M, Mc);
-    const float a = (M > -INFINITY) ? fast_exp2((M - Mn) * kLog2e) : 0.f;
-    acc *= a;
-    ctot *= a;
-    M = Mn;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-      const float c = (mv[u] > -INFINITY) ? fast_exp2((mv[u] - M) * kLog2e) * ev[u] : 0.f;
-      acc += c * v[u];
-      if (f4 == 0) ctot += c;
+      for (int u = 0; u < NU; ++u) {
+        const float c = (mv[u] > -INFINITY) ? fast_exp2((mv[u] - M) * kLog2e) * ev[u] : 0.f;
+        acc += c * v[u];
+        ctot += c;
+      }
     }
   }
-  // total weight: lanes by an xor tree, then waves in order
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) ctot += __shfl_xor(ctot, o);
-  if (lane == 0) red[wv] = ctot;
+  if (f4 == 0) {
+    sm_m[pg] = M;
+    sm_c[pg] = ctot;
+  }
   part[t] = acc;
   __syncthreads();
   if (t < F4) {
+    float Mx = -INFINITY;
+#pragma unroll 8
+    for (int g2 = 0; g2 < PG; ++g2) Mx = fmaxf(Mx, sm_m[g2]);
     float tot = 0.f;
-#pragma unroll
-    for (int i = 0; i < kReduceThreads / 64; ++i) tot += red[i];
-    f32x4 sum = part[t];
-    for (int g2 = 1; g2 < PG; ++g2) sum += part[g2 * F4 + t];
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int g2 = 0; g2 < PG; ++g2) {
+      const float mg = sm_m[g2];
+      const float w = (mg > -INFINITY) ? fast_exp2((mg - Mx) * kLog2e) : 0.f;
+      tot += w * sm_c[g2];
+      sum += w * part[g2 * F4 + t];
+    }
     const float inv = (tot > 0.f) ? 1.f / tot : 0.f;
     T* row = reinterpret_cast<T*>(R.out) + (int64_t)sh * R.D + dc * CW;
     store4<T>(row, 4 * t, sum * inv);
