@@ -705,9 +705,10 @@ __global__ __launch_bounds__(NW * 64) void pa_partition_f32(Params P) {
 // owns float4 t % (CW/4) of the slice and partitions t / (CW/4) + PG*u of
 // each group of PG*NU partitions; all loads of a group are issued at once
 // and folded into the thread's running (max, weight sum, output), rescaled
-// when its max grows; one LDS exchange then merges the per-thread triples. The host picks CW: full rows (one
-// coalesced 1 KB row per wave at D = 256) when there are enough (sequence,
-// head) rows to fill the GPU, narrow slices (more workgroups) otherwise.
+// when its max grows; one LDS exchange then merges the per-thread triples.
+// The host picks CW: full rows (one coalesced 1 KB row per wave at D = 256)
+// when there are enough (sequence, head) rows to fill the GPU, narrow slices
+// (more workgroups) otherwise.
 // With SPEC (small partial sets, where the kernel is latency-bound) the first
 // group's loads go out before the sequence length arrives, bounded by Pmax,
 // and entries past the sequence's partition count are masked afterwards.
