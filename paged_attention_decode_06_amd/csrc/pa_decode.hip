@@ -12,8 +12,10 @@
 //     size once in use; a shape may opt into it (pa_shape.partition_size).
 //
 // Kernel design (gfx950, wave64):
-//   One workgroup per (sequence, KV head, partition); partition is the slowest
-//   grid index so the long single-pass workgroups are dispatched first. Each
+//   One workgroup per work item: (sequence, KV head) for a single pass,
+//   (sequence, KV head, partition) otherwise. Batches map workgroups through
+//   a compact work list built from seq_lens on the device (item_of), with the
+//   long single-pass items first and the unused workgroups at the end. Each
 //   wave walks "tiles" of whole 16-token blocks. For a tile it
 //     - loads K rows so that lane (tok = l%16, grp = l/16) holds 8 consecutive
 //       head dims of token tok: the A operand of a 16x16x32 bf16 MFMA whose M
