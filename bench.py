@@ -35,6 +35,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -57,10 +58,23 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+_CODE_TOKENS = re.compile(r'("(?:\\.|[^"\\\n])*")|//[^\n]*|/\*.*?\*/', re.S)
+
+
+def code_only(text: str) -> str:
+    """C/C++ source with comments removed and whitespace runs collapsed, so
+    that editing a comment does not change a kernel's source hash (string
+    literals, such as inline assembly, are kept as written)."""
+    text = _CODE_TOKENS.sub(lambda m: m.group(1) or " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(paths=None) -> str:
+    """Hash of the code (comments excluded) of the given kernel sources."""
     h = hashlib.sha256()
     for p in (paths or KERNEL_SRCS):
-        h.update(open(p, "rb").read())
+        h.update(code_only(open(p).read()).encode())
+        h.update(b"\0")
     return h.hexdigest()[:16]
 
 
