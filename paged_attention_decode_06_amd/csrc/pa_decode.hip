@@ -116,16 +116,22 @@ __device__ __forceinline__ int clamp_len(const Params& P, int s) {
 __device__ __forceinline__ bool item_of(const Params& P, int b, int lane, int& s_out, int& kvh_out,
                                         int& p_out) {
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes < this one
-  // Pass 1: number of single-pass sequences (AUTO mode; V2 mode has none).
-  int n1 = 0;
-  if (P.mode == PA_MODE_AUTO) {
-    for (int c = 0; c < P.S; c += 64) {
-      const int s = c + lane;
-      const bool one = s < P.S && clamp_len(P, s) <= kThresh;
-      n1 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(one));
-    }
+  // Pass 1, in every workgroup: the number of single-pass sequences (AUTO
+  // mode only) and of partitions, with the length loads of several chunks in
+  // flight at once. Workgroups past the last item leave after this pass.
+  int n1 = 0, np = 0;
+#pragma unroll 4
+  for (int c = 0; c < P.S; c += 64) {
+    const int s = c + lane;
+    const int L = (s < P.S) ? clamp_len(P, s) : -1;
+    const bool one = L >= 0 && P.mode == PA_MODE_AUTO && L <= kThresh;
+    n1 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(one));
+    if (L >= 0 && !one) np += (L + P.PS - 1) / P.PS;
   }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) np += __shfl_xor(np, o);
   const int total1 = n1 * P.Hkv;
+  if (b >= total1 + np * P.Hkv) return false;
   if (b < total1) {
     int r = b / P.Hkv;  // rank of the sequence among the single-pass ones
     for (int c = 0; c < P.S; c += 64) {
