@@ -120,7 +120,7 @@ __device__ __forceinline__ bool item_of(const Params& P, int b, int lane, int& s
   // mode only) and of partitions, with the length loads of several chunks in
   // flight at once. Workgroups past the last item leave after this pass.
   int n1 = 0, np = 0;
-#pragma unroll 4
+#pragma unroll 8
   for (int c = 0; c < P.S; c += 64) {
     const int s = c + lane;
     const int L = (s < P.S) ? clamp_len(P, s) : -1;
@@ -1013,6 +1013,13 @@ hipError_t launch_reduce(const ReduceParams& R, int dtype, const Launch& L) {
   return launch_reduce_t<float>(R, L);
 }
 
+// No sequence can take the partitioned path: V1 forced, or AUTO with a table
+// too narrow for any context to pass the threshold (lengths are clamped to
+// the table's width).
+bool single_pass_only(const pa_shape* sh, int mode) {
+  return mode == PA_MODE_V1 || (mode == PA_MODE_AUTO && (int64_t)sh->max_blocks_per_seq * kBS <= kThresh);
+}
+
 Params make_params(void* out, const void* q, const void* k, const void* v, const int32_t* bt,
                    const int32_t* sl, const pa_shape* sh, float scale, float* es, float* ml,
                    float* to, int mode, int32_t* trace, int32_t* err) {
@@ -1026,7 +1033,7 @@ Params make_params(void* out, const void* q, const void* k, const void* v, const
   // One sequence, or single-pass only: the direct (partition, sequence, KV
   // head) order is already compact. Very large batches keep it too: every
   // workgroup of a compact grid scans all sequence lengths.
-  P.compact = mode != PA_MODE_V1 && P.S > 1 && P.S <= kCompactMaxSeqs && P.Pmax > 1;
+  P.compact = !single_pass_only(sh, mode) && P.S > 1 && P.S <= kCompactMaxSeqs && P.Pmax > 1;
   P.scale2 = scale * kLog2e;
   return P;
 }
@@ -1040,12 +1047,6 @@ ReduceParams make_reduce_params(void* out, const float* es, const float* ml, con
   return R;
 }
 
-// No sequence can take the partitioned path: V1 forced, or AUTO with a table
-// too narrow for any context to pass the threshold (lengths are clamped to
-// the table's width).
-bool single_pass_only(const pa_shape* sh, int mode) {
-  return mode == PA_MODE_V1 || (mode == PA_MODE_AUTO && (int64_t)sh->max_blocks_per_seq * kBS <= kThresh);
-}
 
 int run_partitions(void* out, const void* q, const void* k, const void* v, const int32_t* bt,
                    const int32_t* sl, const pa_shape* sh, float scale, float* es, float* ml,
