@@ -220,6 +220,24 @@ def test_compact_work_list_over_several_chunks(dev, mode):
         assert np.isnan(ml[s_, :, P:]).all() and np.isnan(to[s_, :, P:]).all()   # untouched
 
 
+@pytest.mark.parametrize("S", [600, 1024])
+def test_compact_work_list_large_batches(dev, S):
+    """600 and 1024 sequences: the length pass over 10 and 16 chunks of 64
+    (its unrolled body and its remainder), mostly short contexts with a long
+    partitioned one now and then, in a table 16K tokens wide; every row is
+    checked."""
+    rng = np.random.default_rng(S)
+    lens = rng.integers(0, 301, size=S)
+    long_ = rng.random(S) < 0.03
+    lens[long_] = rng.integers(8193, 12001, size=int(long_.sum()))
+    lens[-1] = 12000
+    cfg = W.DecodeConfig(f"compact{S}", S, 16, 2, 128, "bf16", ("custom",))
+    x = W.make_inputs(cfg, seed=S, seq_lens=lens.tolist(), max_blocks_per_seq=1024)
+    say(f"compact work list: {S} seqs, {int(long_.sum()) + 1} partitioned")
+    out, _ = run(x, dev, "auto")
+    assert_close(x, out, label=f"compact {S}")
+
+
 def test_batch_above_the_work_list_limit(dev):
     """1100 sequences (above the batch size the compact work list serves):
     the grid keeps its direct order; mostly short contexts with a long
