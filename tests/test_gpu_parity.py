@@ -238,6 +238,38 @@ def test_compact_work_list_large_batches(dev, S):
     assert_close(x, out, label=f"compact {S}")
 
 
+def _random_case(i):
+    """Shape and lengths of seeded random case i (sizes the oracle finishes
+    in well under a second)."""
+    rng = np.random.default_rng(5000 + i)
+    dtype = ("bf16", "f16", "f32")[rng.integers(3)]
+    D = int(rng.choice([128, 256]))
+    Hkv = int(rng.choice([1, 2, 4]))
+    G = int(rng.choice([1, 2, 4, 8]))
+    S = int(rng.choice([1, 2, 3, 17, 64, 65, 200]))
+    short = rng.integers(0, 700, size=S)
+    longs = rng.integers(8000, 9400, size=S)      # both sides of the threshold
+    lens = np.where(rng.random(S) < 0.3, longs, short)
+    width = int(rng.choice([0, 700, 2048]))       # 0: the narrowest table
+    width = None if width == 0 else max(width, int(-(-lens.max() // 16)))
+    mode = ("auto", "v1", "v2")[rng.integers(3)]
+    return dtype, D, Hkv, G, S, lens, width, mode
+
+
+@pytest.mark.parametrize("i", range(24))
+def test_random_shapes_vs_oracle(dev, i):
+    """Seeded random shapes: dtype, head_dim, KV heads, group size, batch
+    size (one sequence, several 64-sequence chunks), lengths on both sides of
+    the single-pass threshold, table width and mode; every row against the
+    oracle."""
+    dtype, D, Hkv, G, S, lens, width, mode = _random_case(i)
+    cfg = W.DecodeConfig(f"rand{i}", S, Hkv * G, Hkv, D, dtype, ("custom",))
+    x = W.make_inputs(cfg, seed=5000 + i, seq_lens=lens.tolist(), max_blocks_per_seq=width)
+    say(f"random case {i}: {dtype} D={D} Hkv={Hkv} G={G} S={S} width={x.max_blocks_per_seq} mode={mode}")
+    out, _ = run(x, dev, mode)
+    assert_close(x, out, label=f"random {i} {mode}")
+
+
 def test_batch_above_the_work_list_limit(dev):
     """1100 sequences (above the batch size the compact work list serves):
     the grid keeps its direct order; mostly short contexts with a long
