@@ -106,6 +106,9 @@ __device__ __forceinline__ int work_range(const Params& P, int s, int p, Range& 
 // the 512-token items of 64 mixed-length sequences took 219 us among
 // interleaved empty workgroups and 164 us compact), and the long single-pass
 // items go first so that they do not finish last.
+//
+// clamp_len: sequence s's length as the kernels use it (cut to the table's
+// width, negative lengths read as zero); work_range reports the cut.
 __device__ __forceinline__ int clamp_len(const Params& P, int s) {
   int L = P.sl[s];
   const int cap = P.MB * kBS;
@@ -113,6 +116,7 @@ __device__ __forceinline__ int clamp_len(const Params& P, int s) {
   return L < 0 ? 0 : L;
 }
 
+// item_of: the work item of workgroup b in the compact order described above.
 __device__ __forceinline__ bool item_of(const Params& P, int b, int lane, int& s_out, int& kvh_out,
                                         int& p_out) {
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes < this one
