@@ -7,21 +7,32 @@ in HBM. Before every timed step a 1 GiB scrub *read* evicts the L2s and the
 HBM; the scrub sits outside the timed window (events bracket the decode call
 only). A read scrub leaves no dirty lines behind: a 1 GiB write scrub was
 measured to slow the timed 100K-token step by ~18 us through write-backs that
-compete with the decode's reads. The default workload is the 100K-token decode (1 sequence, 16 query /
-2 KV heads, head_dim 128, bf16, 196 partitions of 512 tokens).
+compete with the decode's reads. The default workload is the 100K-token decode
+(1 sequence, 16 query / 2 KV heads, head_dim 128, bf16, 196 partitions of 512
+tokens).
+
+Timing events: the step's two events are timing-only events
+(hipEventDisableSystemFence, which the HIP runtime documents for timing): a
+default event also writes back and invalidates the caches at system scope when
+it is recorded, which on this GPU adds ~2 us to every marked interval (two
+default events with nothing between them read ~4.3 us, timing-only ones
+~3.2 us). The default-event figure is reported beside it.
 
 Prints ONE JSON line (per workload with --all):
-  value        algorithmic bytes / mean event-timed step time, GB/s
-  ms_per_step  mean cold-cache step time (both kernels and the gap between)
+  value        algorithmic bytes / median event-timed step time, GB/s
+  ms_per_step  median cold-cache step time (both kernels and the gap between)
   roofline     the partition kernel's algorithmic bytes / its mean duration,
                against 8 TB/s. The duration comes from HIP events that the
                library records at the start and the end of that kernel's own
                dispatch (pa_decode_partitions_timed), on the launch stream,
-               over the same scrubbed steps; it reads about 1 us above the
-               profiler's per-dispatch average (the attached events' cost),
-               far less than separate event markers (~5 us).
+               over the same kind of scrubbed steps; it reads about 1 us above
+               the profiler's per-dispatch average (the attached events' cost).
   cpu_baseline the fp64 oracle timed on this host's cores (bounded sample)
 
+--floors measures, on the same workload and buffers, what the decode is up
+against on this GPU: an empty launch, event pairs with nothing between them,
+and a read-only pass over exactly the decode's K/V bytes in its block order
+(include/pa_probe.h) at several workgroup sizes, beside the decode kernels;
 --cold-only runs just the warmup and the timed scrubbed steps (for a
 profiler run whose per-dispatch averages then cover cold calls only);
 --copy-calibration MiB runs a plain device-to-device copy of that size, the
@@ -140,44 +151,64 @@ def moe_traffic_for(num: int, stage: str):
     return None if v is None else int(float(v))
 
 
+def host_cores() -> int:
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
 def cpu_baseline(x, gpu_out, budget_s: float):
-    """Time the fp64 oracle on host cores over a bounded sample of the workload:
-    whole sequences in a fixed random order until the time budget is spent
-    (the workload is repeated when it is shorter than the budget)."""
+    """Time the fp64 oracle on the host's cores over a bounded sample of the
+    workload: whole sequences, one per task on a thread pool sized to the
+    cores this process may run on (each task's matrix products single-threaded,
+    so the pool is what spreads the work), in a fixed random order until the
+    time budget is spent (the workload is repeated when it is shorter)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     import oracle
     from paged_attention_decode_06_amd import workloads as W
     try:
-        from threadpoolctl import threadpool_info
-        blas = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+        from threadpoolctl import threadpool_limits
     except Exception:  # pragma: no cover
-        blas = 1
+        threadpool_limits = None
     c = x.cfg
+    cores = host_cores()
     lists = oracle.gather_list(x.block_tables, x.seq_lens)
-    order = np.random.default_rng(0).permutation(c.num_seqs)
+    order = [int(s) for s in np.random.default_rng(0).permutation(c.num_seqs)]
     got = W.from_device(gpu_out)
-    elapsed, sample_bytes, tokens, visits, reps, worst = 0.0, 0, 0, 0, 0, 0.0
+    elem = 4 if c.dtype == "f32" else 2
+
+    def one(s):
+        return s, oracle.attend_seq(x.q[s], x.k_cache, x.v_cache, lists[s], int(x.seq_lens[s]), x.scale, c.dtype)
+
+    sample_bytes, tokens, visits, worst = 0, 0, 0, 0.0
     checked = set()
-    while elapsed < budget_s and reps < 1000:
-        for s in order:
-            L = int(x.seq_lens[s])
+    limits = threadpool_limits(1) if threadpool_limits else None
+    try:
+        with ThreadPoolExecutor(cores) as ex:
             t0 = time.perf_counter()
-            ref = oracle.attend_seq(x.q[s], x.k_cache, x.v_cache, lists[s], L, x.scale, c.dtype)
-            elapsed += time.perf_counter() - t0
-            if s not in checked:
-                worst = max(worst, float(np.abs(got[s] - ref).max()))
-                checked.add(int(s))
-            sample_bytes += W.algorithmic_bytes([L], c.num_heads, c.num_kv_heads, c.head_dim,
-                                                4 if c.dtype == "f32" else 2)
-            tokens += L
-            visits += 1
-            if elapsed >= budget_s:
-                break
-        reps += 1
+            i = 0
+            while time.perf_counter() - t0 < budget_s and visits < 100000:
+                batch = [order[(i + j) % len(order)] for j in range(cores)]
+                i += cores
+                for s, ref in ex.map(one, batch):
+                    if s not in checked:
+                        worst = max(worst, float(np.abs(got[s] - ref).max()))
+                        checked.add(s)
+                    L = int(x.seq_lens[s])
+                    sample_bytes += W.algorithmic_bytes([L], c.num_heads, c.num_kv_heads, c.head_dim, elem)
+                    tokens += L
+                    visits += 1
+            elapsed = time.perf_counter() - t0
+    finally:
+        if limits is not None:
+            limits.restore_original_limits()
     return {
-        "value": round(sample_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(blas), "kind": "oracle",
+        "value": round(sample_bytes / elapsed / 1e9, 4), "unit": "GB/s", "cores": int(cores), "kind": "oracle",
         "sample": f"fp64 NumPy oracle over {visits} sequence visits ({len(checked)} distinct of {c.num_seqs}, "
-                  f"{tokens} context tokens) in {elapsed:.1f} s; BLAS threads={blas}, "
-                  "gather/softmax loop single-threaded",
+                  f"{tokens} context tokens) in {elapsed:.1f} s on a pool of {cores} threads, one sequence "
+                  "per task, single-threaded BLAS per task",
         "seconds": round(elapsed, 3),
         "max_abs_err_vs_gpu": worst,
     }
@@ -219,34 +250,45 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
         step()
     torch.cuda.synchronize(dev)
 
-    # --- timed region: K steps, each bracketed by events (scrub outside the events)
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    # --- timed region: K steps, each bracketed by timing-only events (scrub outside the events)
+    hev = pa.HipEvents(pa.HipEvents.DISABLE_SYSTEM_FENCE)
+    marks = [(hev.new(), hev.new()) for _ in range(steps)]
     torch.cuda.synchronize(dev)
     wall0 = time.perf_counter()
     for i in range(steps):
         do_scrub(i)
-        ev[i][0].record(stream)
+        hev.record(marks[i][0], stream)
         step()
-        ev[i][1].record(stream)
+        hev.record(marks[i][1], stream)
     torch.cuda.synchronize(dev)
     wall = time.perf_counter() - wall0
-    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    ms = np.array([hev.ms(a, b) for a, b in marks])
     if cold_only:
-        return {"config": workload_label(x, ps), "us_per_step": round(float(ms.mean()) * 1e3, 2)}
+        hev.close()
+        return {"config": workload_label(x, ps), "us_per_step": round(float(np.median(ms)) * 1e3, 2)}
+
+    # --- the same steps between default events (each adds a system-scope cache flush)
+    evd = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        do_scrub(i)
+        evd[i][0].record(stream)
+        step()
+        evd[i][1].record(stream)
+    torch.cuda.synchronize(dev)
+    ms_default = np.array([a.elapsed_time(b) for a, b in evd])
 
     # --- per-kernel durations: the same scrubbed steps, each kernel launched
     #     with events attached to its own dispatch
-    hev = pa.HipEvents()
-    marks = [[hev.new() for _ in range(4)] for _ in range(steps)]
+    kmarks = [[hev.new() for _ in range(4)] for _ in range(steps)]
     for i in range(steps):
         do_scrub(i)
-        a, b, c, d_ = marks[i]
+        a, b, c, d_ = kmarks[i]
         pa.pa_decode_partitions_timed(out, q, kc, vc, bt, sl, x.scale, es, ml, to, pa.MODE_AUTO, a, b,
                                       stream=stream, partition_size=ps)
         pa.pa_lse_reduce_timed(out, es, ml, to, sl, sh, pa.MODE_AUTO, c, d_, stream=stream)
     torch.cuda.synchronize(dev)
-    k1 = np.array([hev.ms(m[0], m[1]) for m in marks])
-    k2 = np.array([hev.ms(m[2], m[3]) for m in marks])
+    k1 = np.array([hev.ms(m[0], m[1]) for m in kmarks])
+    k2 = np.array([hev.ms(m[2], m[3]) for m in kmarks])
     hev.close()
     k1_ms, k2_ms = float(k1.mean()), float(k2.mean())
 
@@ -274,15 +316,17 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
     pipelined_ms = pipelined(partitions, reduce)
 
     # --- warm (cache-resident) figure, labelled as such
-    evw = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    hw = pa.HipEvents(pa.HipEvents.DISABLE_SYSTEM_FENCE)
+    evw = [(hw.new(), hw.new()) for _ in range(steps)]
     for i in range(steps):
-        evw[i][0].record(stream)
+        hw.record(evw[i][0], stream)
         step()
-        evw[i][1].record(stream)
+        hw.record(evw[i][1], stream)
     torch.cuda.synchronize(dev)
-    warm = np.array([a.elapsed_time(b) for a, b in evw])
+    warm = np.array([hw.ms(a, b) for a, b in evw])
+    hw.close()
 
-    ms_step = float(ms.mean())
+    ms_step = float(np.median(ms))
     gbs = step_bytes / (ms_step * 1e-3) / 1e9
     achieved = pk_bytes / (k1_ms * 1e-3) / 1e9
     res = {
@@ -302,8 +346,13 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
         "us_per_step": round(ms_step * 1e3, 2),
         "pct_of_peak": round(100 * gbs / PEAK_GBS, 2),
         "us_per_step_p10_p50_p90": [round(float(np.percentile(ms, p)) * 1e3, 2) for p in (10, 50, 90)],
+        "us_per_step_mean": round(float(ms.mean()) * 1e3, 2),
+        "step_timing": "median of per-step intervals between timing-only events (hipEventDisableSystemFence) "
+                       "recorded before and after pa_decode on the launch stream, each step after a 1 GiB "
+                       "read scrub",
+        "us_per_step_default_events_p50": round(float(np.median(ms_default)) * 1e3, 2),
         "cache_scrub_bytes_per_step": SCRUB_BYTES if scrub else 0,
-        "warm_cache_us_per_step": round(float(warm.mean()) * 1e3, 2),
+        "warm_cache_us_per_step": round(float(np.median(warm)) * 1e3, 2),
         "pipelined_us_per_step": round(pipelined_ms * 1e3, 2),
         "algorithmic_bytes_per_step": int(step_bytes),
         "seq_steps_per_s": round(x.cfg.num_seqs / (ms_step * 1e-3), 1),
@@ -331,6 +380,86 @@ def bench_one(num: int, steps: int, warmup: int, scrub: bool, cpu_budget: float,
         res["cpu_baseline"] = cpu_baseline(x, out, cpu_budget)
     else:
         res["cpu_baseline"] = None
+    del scrub_buf
+    return res
+
+
+def bench_floors(num: int, steps: int, dev) -> dict:
+    """Floors of the decode step on this GPU, on the workload's own buffers:
+    an empty launch, event pairs around nothing, and a read-only pass over
+    exactly the decode's K/V bytes in its block order, beside the decode's
+    partition kernel, its reduce kernel and the whole step. Every figure is
+    the median over `steps` repetitions, each after a 1 GiB read scrub."""
+    import torch
+
+    import oracle
+    import paged_attention_decode_06_amd as pa
+    from paged_attention_decode_06_amd import workloads as W
+
+    x = W.make_inputs(num)
+    d = W.to_device(x, dev)
+    q, kc, vc, bt, sl = d["q"], d["k_cache"], d["v_cache"], d["block_tables"], d["seq_lens"]
+    out = torch.empty_like(q)
+    sh = pa.make_shape(q, kc, bt)
+    es, ml, to = pa.alloc_partials(sh, dev)
+    elem = 4 if x.cfg.dtype == "f32" else 2
+    kv_bytes = 2 * int(x.seq_lens.astype(np.int64).sum()) * x.cfg.num_kv_heads * x.cfg.head_dim * elem
+    # the decode's block order: every sequence's gather list, concatenated (each at every KV head)
+    ids_host = np.concatenate([np.asarray(b, dtype=np.int32) for b in oracle.gather_list(x.block_tables, x.seq_lens)])
+    ids = torch.from_numpy(ids_host).to(dev)
+    scrub_buf = torch.empty(SCRUB_BYTES // 4, dtype=torch.float32, device=dev)
+    sink1 = torch.empty((), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    hev = pa.HipEvents(pa.HipEvents.DISABLE_SYSTEM_FENCE)
+
+    def median_us(fn, attached: bool, scrub=True):
+        ts = []
+        for i in range(steps + 3):
+            if scrub:
+                torch.sum(scrub_buf, dim=None, out=sink1)
+            a, b = hev.new(), hev.new()
+            if attached:
+                fn(a, b)
+            else:
+                hev.record(a, stream)
+                fn(None, None)
+                hev.record(b, stream)
+            torch.cuda.synchronize(dev)
+            if i >= 3:
+                ts.append(hev.ms(a, b) * 1e3)
+        return round(float(np.median(ts)), 2)
+
+    res = {"metric": "decode-step floors on this GPU (us, medians)", "config": workload_label(x),
+           "kv_bytes": kv_bytes, "steps": steps}
+    res["two_timing_only_events_nothing_between"] = median_us(lambda a, b: None, False)
+    res["empty_kernel_between_events"] = median_us(lambda a, b: pa.pa_probe_empty(stream=stream), False)
+    res["empty_kernel_attached_events"] = median_us(lambda a, b: pa.pa_probe_empty(a, b, stream=stream), True)
+    reads = {}
+    for per in (2, 4, 8, 16, 32):
+        grid = pa.probe_read_grid(ids.numel(), x.cfg.num_kv_heads, per)
+        sink = torch.empty((grid,), dtype=torch.int32, device=dev)
+        t = median_us(lambda a, b: pa.pa_probe_paged_read(kc, vc, ids, per, sink, a, b, stream=stream), True)
+        reads[f"blocks_per_workgroup_{per}"] = {"workgroups": grid, "us_attached": t,
+                                                "GB_s": round(kv_bytes / (t * 1e-6) / 1e9, 1)}
+    res["paged_read_probe"] = reads
+    best = min(v["us_attached"] for v in reads.values())
+    res["paged_read_floor_us_attached"] = best
+    part = lambda a, b: pa.pa_decode_partitions_timed(out, q, kc, vc, bt, sl, x.scale, es, ml, to, pa.MODE_AUTO,
+                                                      a, b, stream=stream)
+    res["partition_kernel_attached"] = median_us(part, True)
+    red = lambda a, b: pa.pa_lse_reduce_timed(out, es, ml, to, sl, sh, pa.MODE_AUTO, a, b, stream=stream)
+    res["reduce_kernel_attached"] = median_us(red, True)
+    res["step_between_events"] = median_us(
+        lambda a, b: pa.pa_decode(out, q, kc, vc, bt, sl, x.scale, es, ml, to, stream=stream), False)
+    res["partition_kernel_between_events"] = median_us(
+        lambda a, b: pa.pa_decode_partitions(out, q, kc, vc, bt, sl, x.scale, es, ml, to, pa.MODE_AUTO,
+                                             stream=stream), False)
+    best_per = min((2, 4, 8, 16, 32), key=lambda p_: reads[f"blocks_per_workgroup_{p_}"]["us_attached"])
+    best_sink = torch.empty((pa.probe_read_grid(ids.numel(), x.cfg.num_kv_heads, best_per),), dtype=torch.int32,
+                            device=dev)
+    res["paged_read_best_between_events"] = median_us(
+        lambda a, b: pa.pa_probe_paged_read(kc, vc, ids, best_per, best_sink, stream=stream), False)
+    hev.close()
     del scrub_buf
     return res
 
@@ -566,6 +695,8 @@ def main(argv=None):
     ap.add_argument("--moe", type=int, default=0, metavar="N",
                     help="measure MoE routing workload N (1: 16384 tokens, 2: 256 tokens); --all-moe for both")
     ap.add_argument("--all-moe", action="store_true", help="every MoE routing workload, one JSON line each")
+    ap.add_argument("--floors", action="store_true",
+                    help="measure the step's floors on this GPU (empty launch, event pairs, read-only pass)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB MiB (counter calibration) and exit")
     args = ap.parse_args(argv)
@@ -601,6 +732,10 @@ def main(argv=None):
         for n in ([1, 2, 3, 4] if args.all_prefill else [args.prefill]):
             res = bench_prefill(n, args.steps, args.warmup, not args.no_scrub, args.cpu_budget, dev)
             print(json.dumps(res), flush=True)
+        return 0
+    if args.floors:
+        for n in ([1, 2, 3, 4, 5] if args.all else [args.config]):
+            print(json.dumps(bench_floors(n, args.steps, dev)), flush=True)
         return 0
     nums = [1, 2, 3, 4, 5] if args.all else [args.config]
     for n in nums:

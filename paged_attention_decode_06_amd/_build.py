@@ -8,7 +8,8 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 SRC = os.path.join(HERE, "csrc", "pa_decode.hip")
-SOURCES = [SRC, os.path.join(HERE, "csrc", "pa_prefill.hip"), os.path.join(HERE, "csrc", "pa_moe.hip")]
+SOURCES = [SRC, os.path.join(HERE, "csrc", "pa_prefill.hip"), os.path.join(HERE, "csrc", "pa_moe.hip"),
+           os.path.join(HERE, "csrc", "pa_probe.hip")]
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libpa_decode.so")
 ARCH = "gfx950"

@@ -13,7 +13,8 @@ import re
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libpa_decode.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "pa_decode.h")
-HEADERS = [HEADER, os.path.join(os.path.dirname(HERE), "include", "pa_moe.h")]
+HEADERS = [HEADER, os.path.join(os.path.dirname(HERE), "include", "pa_moe.h"),
+           os.path.join(os.path.dirname(HERE), "include", "pa_probe.h")]
 
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 MODE_AUTO, MODE_V1, MODE_V2 = 0, 1, 2
@@ -69,6 +70,10 @@ _SIGS = {
     "pa_moe_combine": (ctypes.c_int, [_P, _P, _P, _P, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                       ctypes.c_int32, _P]),
     "pa_partials_elems": (ctypes.c_int64, [ctypes.POINTER(PaShape), ctypes.c_int]),
+    "pa_probe_empty": (ctypes.c_int, [_P, _P, _P]),
+    "pa_probe_paged_read": (ctypes.c_int, [_P, _P, _P, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                           ctypes.c_int64, ctypes.c_int32, _P, ctypes.c_int64, _P, _P, _P]),
+    "pa_probe_paged_read_grid": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int32, ctypes.c_int32]),
     "pa_check_args": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), _P, _P, _P, ctypes.c_int]),
     "pa_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "pa_version": (ctypes.c_int, []),
@@ -187,6 +192,38 @@ def _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens, partials=()
             raise PaError(PA_EINVAL, "partial buffers must be float32")
 
 
+def check_sizes(shape: PaShape, out=None, seq_lens=None, partials=None, q=None, k_cache=None) -> None:
+    """Element counts of the decode buffers against `shape`, before any launch.
+
+    seq_lens must hold num_seqs entries, out (and q) num_seqs * num_heads *
+    head_dim, the caches [num_blocks, num_kv_heads, 16, head_dim], and the
+    partial buffers (exp_sums, max_logits, tmp_out) num_seqs * num_heads *
+    Pmax (* head_dim) with Pmax the partition count of this very shape (its
+    partition size included). Raises PaError(PA_EINVAL) on a mismatch, which
+    would otherwise let a kernel write past the end of a buffer."""
+    S, H, D = int(shape.num_seqs), int(shape.num_heads), int(shape.head_dim)
+    if seq_lens is not None and seq_lens.numel() != S:
+        raise PaError(PA_EINVAL, f"seq_lens holds {seq_lens.numel()} entries for {S} sequences")
+    for name, t in (("out", out), ("q", q)):
+        if t is not None and t.numel() != S * H * D:
+            raise PaError(PA_EINVAL, f"{name} holds {t.numel()} elements, the shape needs {S * H * D}")
+    if k_cache is not None and tuple(k_cache.shape) != (int(shape.num_blocks), int(shape.num_kv_heads),
+                                                        int(shape.block_size), D):
+        raise PaError(PA_EINVAL, f"cache shape {tuple(k_cache.shape)} does not match the shape")
+    if partials is not None:
+        P = (int(shape.max_blocks_per_seq) * int(shape.block_size) + _psize(shape) - 1) // _psize(shape)
+        es, ml, to = partials
+        for name, t, n in (("exp_sums", es, S * H * P), ("max_logits", ml, S * H * P),
+                           ("tmp_out", to, S * H * P * D)):
+            if t is not None and t.numel() != n:
+                raise PaError(PA_EINVAL, f"{name} holds {t.numel()} elements, the shape needs {n} "
+                                         f"({P} partitions of {_psize(shape)} tokens)")
+
+
+def _psize(shape: PaShape) -> int:
+    return int(shape.partition_size) if int(shape.partition_size) else PARTITION_SIZE
+
+
 def _call(name, rc):
     if rc != PA_OK:
         raise PaError(rc, name)
@@ -211,6 +248,7 @@ def alloc_partials(shape: PaShape, device):
 def pa_decode_v1(out, q, k_cache, v_cache, block_tables, seq_lens, scale, stream=None):
     _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens)
     sh = make_shape(q, k_cache, block_tables)
+    check_sizes(sh, out=out, seq_lens=seq_lens, q=q, k_cache=k_cache)
     _call("pa_decode_v1", load().pa_decode_v1(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                               _ptr(block_tables), _ptr(seq_lens), ctypes.byref(sh),
                                               float(scale), _stream(stream, q.device)))
@@ -220,6 +258,7 @@ def _full(name, out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sum
           partition_size):
     _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens, (exp_sums, max_logits, tmp_out))
     sh = make_shape(q, k_cache, block_tables, partition_size)
+    check_sizes(sh, out=out, seq_lens=seq_lens, partials=(exp_sums, max_logits, tmp_out), q=q, k_cache=k_cache)
     fn = getattr(load(), name)
     _call(name, fn(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
                    ctypes.byref(sh), float(scale), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out),
@@ -242,6 +281,7 @@ def pa_decode_partitions(out, q, k_cache, v_cache, block_tables, seq_lens, scale
                          tmp_out, mode, stream=None, partition_size=0):
     _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens, (exp_sums, max_logits, tmp_out))
     sh = make_shape(q, k_cache, block_tables, partition_size)
+    check_sizes(sh, out=out, seq_lens=seq_lens, partials=(exp_sums, max_logits, tmp_out), q=q, k_cache=k_cache)
     _call("pa_decode_partitions", load().pa_decode_partitions(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
         ctypes.byref(sh), float(scale), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), int(mode),
@@ -252,6 +292,7 @@ def pa_decode_partitions_debug(out, q, k_cache, v_cache, block_tables, seq_lens,
                                tmp_out, mode, gather_trace=None, err_flag=None, stream=None, partition_size=0):
     _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens, (exp_sums, max_logits, tmp_out))
     sh = make_shape(q, k_cache, block_tables, partition_size)
+    check_sizes(sh, out=out, seq_lens=seq_lens, partials=(exp_sums, max_logits, tmp_out), q=q, k_cache=k_cache)
     _call("pa_decode_partitions_debug", load().pa_decode_partitions_debug(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
         ctypes.byref(sh), float(scale), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), int(mode),
@@ -260,6 +301,7 @@ def pa_decode_partitions_debug(out, q, k_cache, v_cache, block_tables, seq_lens,
 
 def pa_lse_reduce(out, exp_sums, max_logits, tmp_out, seq_lens, shape: PaShape, mode=MODE_V2, stream=None):
     _check_tensors(out, None, None, None, None, seq_lens, (exp_sums, max_logits, tmp_out))
+    check_sizes(shape, out=out, seq_lens=seq_lens, partials=(exp_sums, max_logits, tmp_out))
     _call("pa_lse_reduce", load().pa_lse_reduce(_ptr(out), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out),
                                                 _ptr(seq_lens), ctypes.byref(shape), int(mode),
                                                 _stream(stream, out.device)))
@@ -270,6 +312,7 @@ def pa_decode_partitions_timed(out, q, k_cache, v_cache, block_tables, seq_lens,
     """Phase 1 with raw hipEvent_t handles (ints) recorded around the kernel itself."""
     _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens, (exp_sums, max_logits, tmp_out))
     sh = make_shape(q, k_cache, block_tables, partition_size)
+    check_sizes(sh, out=out, seq_lens=seq_lens, partials=(exp_sums, max_logits, tmp_out), q=q, k_cache=k_cache)
     _call("pa_decode_partitions_timed", load().pa_decode_partitions_timed(
         _ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache), _ptr(block_tables), _ptr(seq_lens),
         ctypes.byref(sh), float(scale), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), int(mode),
@@ -280,6 +323,7 @@ def pa_lse_reduce_timed(out, exp_sums, max_logits, tmp_out, seq_lens, shape: PaS
                         stop_event, stream=None):
     """Phase 2 with raw hipEvent_t handles (ints) recorded around the kernel itself."""
     _check_tensors(out, None, None, None, None, seq_lens, (exp_sums, max_logits, tmp_out))
+    check_sizes(shape, out=out, seq_lens=seq_lens, partials=(exp_sums, max_logits, tmp_out))
     _call("pa_lse_reduce_timed", load().pa_lse_reduce_timed(
         _ptr(out), _ptr(exp_sums), _ptr(max_logits), _ptr(tmp_out), _ptr(seq_lens), ctypes.byref(shape),
         int(mode), ctypes.c_void_p(start_event), ctypes.c_void_p(stop_event), _stream(stream, out.device)))
@@ -370,6 +414,33 @@ def pa_moe_combine(out, y_sorted, topk_weights, pair_pos, stream=None):
                                                   Hd, _dtype_code(out.dtype), _stream(stream, out.device)))
 
 
+# ---------------------------------------------------------------- measurement kernels
+def pa_probe_empty(start=None, stop=None, stream=None):
+    """An empty launch (one wave), optionally with events attached to its dispatch."""
+    import torch
+    sp = _stream(stream, torch.device("cuda", torch.cuda.current_device()))
+    _call("pa_probe_empty", load().pa_probe_empty(ctypes.c_void_p(start), ctypes.c_void_p(stop), sp))
+
+
+def probe_read_grid(num_ids: int, num_kv_heads: int, units_per_wg: int) -> int:
+    r = int(load().pa_probe_paged_read_grid(int(num_ids), int(num_kv_heads), int(units_per_wg)))
+    _call("pa_probe_paged_read_grid", r if r < 0 else 0)
+    return r
+
+
+def pa_probe_paged_read(k_cache, v_cache, block_ids, units_per_wg, sink, start=None, stop=None, stream=None):
+    """Read-only pass over the K/V bytes of `block_ids` (int32, every KV head), no math."""
+    import torch
+    _gpu_contig(k_cache, v_cache, block_ids, sink)
+    if block_ids.dtype != torch.int32 or sink.dtype != torch.int32:
+        raise PaError(PA_EINVAL, "block_ids and sink must be int32")
+    NB, Hkv, BS, D = k_cache.shape
+    _call("pa_probe_paged_read", load().pa_probe_paged_read(
+        _ptr(k_cache), _ptr(v_cache), _ptr(block_ids), int(block_ids.numel()), int(Hkv), int(D),
+        int(k_cache.element_size()), int(NB), int(units_per_wg), _ptr(sink), int(sink.numel()),
+        ctypes.c_void_p(start), ctypes.c_void_p(stop), _stream(stream, k_cache.device)))
+
+
 class HipEvents:
     """Raw hipEvent_t handles for the *_timed entry points.
 
@@ -378,21 +449,34 @@ class HipEvents:
     second copy. They are freed by close().
     """
 
-    def __init__(self):
+    # hipEventCreateWithFlags: a timing-only event that records without a
+    # system-scope cache write-back and invalidate (the HIP runtime documents
+    # this flag for precise timing; the decode's results stay on the device).
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, flags: int = 0):
         load()  # maps the runtime the library is linked against
         self.ct = ctypes
+        self.flags = int(flags)
         self.hip = ctypes.CDLL("libamdhip64.so.7", mode=os.RTLD_NOLOAD | os.RTLD_GLOBAL)
-        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.made = []
 
     def new(self) -> int:
         h = self.ct.c_void_p()
-        if self.hip.hipEventCreate(self.ct.byref(h)) != 0:
-            raise RuntimeError("hipEventCreate failed")
+        if self.hip.hipEventCreateWithFlags(self.ct.byref(h), self.flags) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
         self.made.append(h.value)
         return h.value
+
+    def record(self, event: int, stream) -> None:
+        """Record `event` on a torch stream (or a raw hipStream_t int)."""
+        sp = getattr(stream, "cuda_stream", stream)
+        if self.hip.hipEventRecord(self.ct.c_void_p(event), self.ct.c_void_p(int(sp))) != 0:
+            raise RuntimeError("hipEventRecord failed")
 
     def ms(self, a: int, b: int) -> float:
         out = self.ct.c_float()

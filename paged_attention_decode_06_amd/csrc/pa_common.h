@@ -34,12 +34,8 @@ __device__ __forceinline__ u32x4 ld16(const void* p) {
 // Loads of the K/V stream (each byte is read once per call) carry the
 // non-temporal hint: measured 6-10% faster than plain loads on the largest
 // batch (pure reads reach ~6.4 TB/s that way).
-#ifndef PA_NT_KV
-#define PA_NT_KV 1
-#endif
 __device__ __forceinline__ u32x4 ld16_stream(const void* p) {
-  if constexpr (PA_NT_KV) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  else return *reinterpret_cast<const u32x4*>(p);
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -158,6 +154,56 @@ __device__ __forceinline__ void issue_tile(BTile<D, TB>& T, const E* kbase, cons
           T.v[b][rr][h] = (u32x4){0u, 0u, 0u, 0u};
         }
     }
+  }
+}
+
+// Buffer resource over one (block, KV head) of a cache: `bytes` long, 0 for a
+// block outside the context. Loads through a zero-length resource return
+// zeros without touching memory, so a tile's loads need no branch. `base`
+// and `bytes` must be the same in every lane of the wave (a resource lives in
+// scalar registers); readfirstlane states that to the compiler, which would
+// otherwise loop over the lanes' values.
+constexpr uint32_t kBufferWord3 = 0x00020000;  // gfx9: 32-bit data format, raw access
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(base);
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  void* ua = reinterpret_cast<void*>(lo | (hi << 32));
+  return __builtin_amdgcn_make_buffer_rsrc(ua, (short)0, (int)__builtin_amdgcn_readfirstlane(bytes),
+                                           (int)kBufferWord3);
+}
+constexpr int kAuxNT = 2;  // cache-policy bits of a buffer load: non-temporal
+
+// Same tile as issue_tile, with branch-free loads: a block with valid[b]
+// false reads as zeros and costs no memory traffic. Every wave issues the
+// same instructions for every tile, which keeps the compiler's wait counts
+// exact when several tiles are in flight.
+template <typename E, int D, int TB>
+__device__ __forceinline__ void issue_tile_rsrc(BTile<D, TB>& T, const E* kbase, const E* vbase,
+                                                int64_t block_elems, const int64_t (&phys)[TB],
+                                                const bool (&valid)[TB], int g, int grp) {
+  constexpr int NH = D / 128;
+  constexpr uint32_t kBytes = (uint32_t)(kBS * D * sizeof(E));
+#pragma unroll
+  for (int b = 0; b < TB; ++b) {
+    const int64_t off = valid[b] ? phys[b] * block_elems : 0;
+    const uint32_t n = valid[b] ? kBytes : 0u;
+    const __amdgpu_buffer_rsrc_t kr = block_rsrc(kbase + off, n);
+    const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + off, n);
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int byte = (int)((((4 * grp + rr) * D) + h * 128 + 8 * g) * sizeof(E));
+        T.k[b][rr][h] = __builtin_amdgcn_raw_buffer_load_b128(kr, byte, 0, kAuxNT);
+      }
+#pragma unroll
+    for (int rr = 0; rr < 4; ++rr)
+#pragma unroll
+      for (int h = 0; h < NH; ++h) {
+        const int byte = (int)((((4 * grp + rr) * D) + h * 128 + 8 * g) * sizeof(E));
+        T.v[b][rr][h] = __builtin_amdgcn_raw_buffer_load_b128(vr, byte, 0, kAuxNT);
+      }
   }
 }
 

@@ -34,6 +34,7 @@
 // through the optional error word).
 
 #include <algorithm>
+#include <atomic>
 
 #include "pa_common.h"
 
@@ -121,16 +122,27 @@ __device__ __forceinline__ bool item_of(const Params& P, int b, int lane, int& s
                                         int& p_out) {
   const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));  // lanes < this one
   // Pass 1, in every workgroup: the number of single-pass sequences (AUTO
-  // mode only) and of partitions, with the length loads of several chunks in
-  // flight at once. Workgroups past the last item leave after this pass.
+  // mode only) and of partitions. The lengths of eight 64-sequence chunks are
+  // loaded into registers before any of them is used, so their loads are in
+  // flight together. Workgroups past the last item leave after this pass.
+  constexpr int kLenChunks = 8;
   int n1 = 0, np = 0;
-#pragma unroll 8
-  for (int c = 0; c < P.S; c += 64) {
-    const int s = c + lane;
-    const int L = (s < P.S) ? clamp_len(P, s) : -1;
-    const bool one = L >= 0 && P.mode == PA_MODE_AUTO && L <= kThresh;
-    n1 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(one));
-    if (L >= 0 && !one) np += (L + P.PS - 1) / P.PS;
+  for (int c0 = 0; c0 < P.S; c0 += kLenChunks * 64) {
+    int len[kLenChunks];
+#pragma unroll
+    for (int u = 0; u < kLenChunks; ++u)  // unconditional loads (index clamped into the batch)
+      len[u] = P.sl[min(c0 + 64 * u + lane, P.S - 1)];
+#pragma unroll
+    for (int u = 0; u < kLenChunks; ++u) {
+      const int L = len[u] > P.MB * kBS ? P.MB * kBS : len[u];
+      len[u] = (c0 + 64 * u + lane < P.S) ? (L < 0 ? 0 : L) : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kLenChunks; ++u) {
+      const bool one = len[u] >= 0 && P.mode == PA_MODE_AUTO && len[u] <= kThresh;
+      n1 += __builtin_popcountll(__builtin_amdgcn_ballot_w64(one));
+      if (len[u] >= 0 && !one) np += (len[u] + P.PS - 1) / P.PS;
+    }
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) np += __shfl_xor(np, o);
@@ -210,11 +222,13 @@ __device__ __forceinline__ void store4_partial(float* row, int d, f32x4 v) {
 // dim_of(a, i) names the head dim held in acc[a][i] (dims a..a+3 of one i are
 // consecutive for a multiple of 4).
 //
-// Every wave rescales its output to the workgroup max and stores it in LDS
-// as [wave][head][D] rows; then all threads sum the waves in a fixed order
-// (bitwise deterministic) and write whole output rows with consecutive
-// 16-byte stores, so every row goes out as full cache lines: rows written in
-// scattered 16-byte pieces measured about 15% slower on the largest batch.
+// Every wave stores its (max, exp-sum) and its unscaled output rows in its
+// own LDS area ([wave][head][D] rows, apart from the main loop's scratch, so
+// no wave waits for another before writing); after one barrier all threads
+// rescale and sum the waves in a fixed order (bitwise deterministic) and
+// write whole output rows with consecutive 16-byte stores, so every row goes
+// out as full cache lines: rows written in scattered 16-byte pieces measured
+// about 15% slower on the largest batch.
 template <typename T, int D, int NACC, int NW, typename DimOf>
 __device__ __forceinline__ void merge_and_write(const Params& P, const Range& r, int s, int kvh,
                                                 int p, int w, int lane, const f32x4 (&acc)[NACC],
@@ -229,19 +243,13 @@ __device__ __forceinline__ void merge_and_write(const Params& P, const Range& r,
     sm_m[w * 16 + g] = m;
     sm_l[w * 16 + g] = lsum;
   }
-  __syncthreads();  // also: every wave has left its main loop, so sm_o may reuse its scratch
-  float M = -INFINITY;
-#pragma unroll
-  for (int i = 0; i < NW; ++i) M = fmaxf(M, sm_m[i * 16 + g]);
-  const float f = (m > -INFINITY) ? fast_exp2(m - M) : 0.f;
   if (g < G) {
     float* row = sm_o + ((size_t)w * G + g) * RS;
 #pragma unroll
     for (int a = 0; a < NACC; a += 4)
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<f32x4*>(row + dim_of(a, i)) =
-            (f32x4){acc[a][i] * f, acc[a + 1][i] * f, acc[a + 2][i] * f, acc[a + 3][i] * f};
+        *reinterpret_cast<f32x4*>(row + dim_of(a, i)) = (f32x4){acc[a][i], acc[a + 1][i], acc[a + 2][i], acc[a + 3][i]};
   }
   __syncthreads();
   const int t = threadIdx.x;
@@ -255,8 +263,9 @@ __device__ __forceinline__ void merge_and_write(const Params& P, const Range& r,
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       const float mi = sm_m[i * 16 + hg];
-      lt += (mi > -INFINITY) ? sm_l[i * 16 + hg] * fast_exp2(mi - Mg) : 0.f;
-      sum += *reinterpret_cast<const f32x4*>(sm_o + ((size_t)i * G + hg) * RS + d);
+      const float f = (mi > -INFINITY) ? fast_exp2(mi - Mg) : 0.f;
+      lt += sm_l[i * 16 + hg] * f;
+      sum += f * *reinterpret_cast<const f32x4*>(sm_o + ((size_t)i * G + hg) * RS + d);
     }
     const float inv = 1.f / lt;
     const int64_t sh = (int64_t)s * P.H + kvh * G + hg;
@@ -322,25 +331,13 @@ __device__ __forceinline__ int check_block_ids(const Params& P, int id, int s, c
   return id;
 }
 
-// Keep the QK B operand (q of the GQA group) in LDS instead of registers.
-#ifndef PA_D128_Q_LDS
-#define PA_D128_Q_LDS 0
-#endif
-#ifndef PA_D256_Q_LDS
-#define PA_D256_Q_LDS 0
-#endif
-
-// Minimum waves per SIMD the register allocation must allow, per head_dim.
-#ifndef PA_D128_WAVES_PER_EU
-#define PA_D128_WAVES_PER_EU 3
-#endif
-#ifndef PA_D256_WAVES_PER_EU
-#define PA_D256_WAVES_PER_EU 2
-#endif
-
-template <typename T, int D, int NW, int TB, int PF, bool TRACE>
-__global__ __launch_bounds__(NW * 64)
-__attribute__((amdgpu_waves_per_eu(D == 128 ? PA_D128_WAVES_PER_EU : PA_D256_WAVES_PER_EU)))
+// NBUF: tiles of the wave in flight at once. Each wave keeps a ring of NBUF
+// register tiles: the loads of tiles k+1 .. k+NBUF-1 are outstanding while
+// tile k is computed, and tile k's buffer takes the loads of tile k+NBUF as
+// soon as its math is done. WPE: the waves per SIMD the register allocation
+// must allow (a deeper ring needs fewer, larger waves).
+template <typename T, int D, int NW, int TB, int NBUF, int CT, int WPE, bool TRACE>
+__global__ __launch_bounds__(NW * 64) __attribute__((amdgpu_waves_per_eu(WPE)))
 void pa_partition_h16(Params P) {
   typedef typename H16<T>::x8 tx8;
   typedef typename H16<T>::x4 tx4;
@@ -350,7 +347,7 @@ void pa_partition_h16(Params P) {
   constexpr int NACC = NH * 8;  // output tiles: (h, j) -> dims 128h + 8m + j
   constexpr int CH = 64 / TB;   // tiles per block-id refill
   constexpr int KCH = D / 8;    // 16-byte chunks per K row
-  constexpr bool QLDS = (D == 128) ? PA_D128_Q_LDS : PA_D256_Q_LDS;
+  static_assert(NBUF >= 1 && NBUF <= CT && CH % CT == 0, "ring depth and chunk size");
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane & 15, grp = lane >> 4;
@@ -375,36 +372,20 @@ void pa_partition_h16(Params P) {
     return;
   }
 
-  // LDS: [wave max | wave exp-sum][q operand (QLDS)][per-wave K tiles]; the
-  // merge reuses everything after the first two arrays.
-  u32x4* qlds = reinterpret_cast<u32x4*>(smem + 2 * NW * 16);
-  u32x4* ktile = qlds + (QLDS ? KK * 64 : 0) + (size_t)w * TB * 16 * KCH;
+  // LDS: [wave max | wave exp-sum][merge rows: NW x G x (D + 4) floats][per-wave K tiles].
+  u32x4* ktile = reinterpret_cast<u32x4*>(smem + 2 * NW * 16 + (size_t)NW * P.G * (D + 4)) + (size_t)w * TB * 16 * KCH;
 
-  // B operand of the QK MFMA: lane holds q[head g][kk*32 + 8*grp .. +8],
-  // either in registers or (QLDS) in LDS as [kk][lane], written once here.
-  tx8 qv[QLDS ? 1 : KK];
+  // B operand of the QK MFMA: lane holds q[head g][kk*32 + 8*grp .. +8].
+  tx8 qv[KK];
   {
     const T* qrow = reinterpret_cast<const T*>(P.q) + ((int64_t)s * P.H + kvh * P.G + g) * D;
-    if constexpr (QLDS) {
-      for (int kk = w; kk < KK; kk += NW) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (g < P.G) x = ld16(qrow + kk * 32 + grp * 8);
-        qlds[kk * 64 + lane] = x;
-      }
-      __syncthreads();
-    } else {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        u32x4 x = {0u, 0u, 0u, 0u};
-        if (g < P.G) x = ld16(qrow + kk * 32 + grp * 8);
-        qv[kk] = __builtin_bit_cast(tx8, x);
-      }
+    for (int kk = 0; kk < KK; ++kk) {
+      u32x4 x = {0u, 0u, 0u, 0u};
+      if (g < P.G) x = ld16(qrow + kk * 32 + grp * 8);
+      qv[kk] = __builtin_bit_cast(tx8, x);
     }
   }
-  auto q_operand = [&](int kk) -> tx8 {
-    if constexpr (QLDS) return __builtin_bit_cast(tx8, qlds[kk * 64 + lane]);
-    else return qv[kk];
-  };
 
   const int64_t head_elems = (int64_t)kBS * D;     // one (block, kv head)
   const int64_t block_elems = head_elems * P.Hkv;  // one physical block
@@ -418,20 +399,6 @@ void pa_partition_h16(Params P) {
 
   const int ntiles = (r.blk_end - r.blk_begin + TB - 1) / TB;
   ids = check_block_ids<TRACE, TB>(P, ids, s, r, t0, dt, 0, lane);
-
-  // block ids and validity of tile t (the wave's k-th tile); refills the id
-  // list at the start of every later CH-tile chunk.
-  auto tile_ids = [&](int t, int64_t (&phys)[TB], bool (&valid)[TB]) {
-    const int k = (t - t0) / dt;
-    if (k > 0 && k % CH == 0)
-      ids = check_block_ids<TRACE, TB>(P, read_block_ids<TB>(P, bt_row, r.blk_begin, t0, dt, k, lane),
-                                       s, r, t0, dt, k, lane);
-#pragma unroll
-    for (int b = 0; b < TB; ++b) {
-      valid[b] = r.blk_begin + t * TB + b < r.blk_end;
-      phys[b] = __builtin_amdgcn_readlane(ids, (k % CH) * TB + b);
-    }
-  };
 
   auto compute = [&](BTile<D, TB>& tl, int t) {
     // K: registers -> swizzled LDS tile -> MFMA operand layout.
@@ -452,7 +419,7 @@ void pa_partition_h16(Params P) {
       for (int kk = 0; kk < KK; ++kk) {
         const int c16 = 4 * kk + grp;
         const u32x4 kr = ktile[(b * 16 + g) * KCH + (c16 ^ g)];
-        sc[b] = H16<T>::mma32(__builtin_bit_cast(tx8, kr), q_operand(kk), sc[b]);
+        sc[b] = H16<T>::mma32(__builtin_bit_cast(tx8, kr), qv[kk], sc[b]);
       }
     }
 
@@ -550,39 +517,35 @@ void pa_partition_h16(Params P) {
     }
   };
 
-  if (t0 < ntiles) {
-    BTile<D, TB> A, B;
-    int64_t phys[TB];
-    bool valid[TB];
-    tile_ids(t0, phys, valid);
-    issue_tile<T, D, TB>(A, kbase, vbase, block_elems, phys, valid, g, grp);
-    if constexpr (PF) {
-      // Two register stages, unrolled so that A and B swap roles without copies.
-      for (int t = t0;;) {
-        const int t1 = t + dt;
-        if (t1 < ntiles) {
-          tile_ids(t1, phys, valid);
-          issue_tile<T, D, TB>(B, kbase, vbase, block_elems, phys, valid, g, grp);
-        }
-        compute(A, t);
-        if (t1 >= ntiles) break;
-        const int t2 = t1 + dt;
-        if (t2 < ntiles) {
-          tile_ids(t2, phys, valid);
-          issue_tile<T, D, TB>(A, kbase, vbase, block_elems, phys, valid, g, grp);
-        }
-        compute(B, t1);
-        if (t2 >= ntiles) break;
-        t = t2;
+  // The wave's tiles go in chunks of CT, each chunk straight-line code with
+  // NBUF tiles in flight: tile k's buffer takes the loads of tile k + NBUF
+  // once tile k is computed. A partition is one chunk; a long single pass
+  // takes several, with the ring refilled at the start of each. Tiles past
+  // the item's end load nothing (zero-length resources) and skip the math.
+  const int nk = t0 < ntiles ? (ntiles - t0 + dt - 1) / dt : 0;  // this wave's tiles
+  for (int k0 = 0; k0 < nk; k0 += CT) {
+    auto issue = [&](BTile<D, TB>& tl, int k) {
+      int64_t phys[TB];
+      bool valid[TB];
+      const int t = t0 + k * dt;
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        valid[b] = k < nk && r.blk_begin + t * TB + b < r.blk_end;
+        phys[b] = __builtin_amdgcn_readlane(ids, (k % CH) * TB + b);
       }
-    } else {
-      for (int t = t0;;) {
-        compute(A, t);
-        t += dt;
-        if (t >= ntiles) break;
-        tile_ids(t, phys, valid);
-        issue_tile<T, D, TB>(A, kbase, vbase, block_elems, phys, valid, g, grp);
-      }
+      issue_tile_rsrc<T, D, TB>(tl, kbase, vbase, block_elems, phys, valid, g, grp);
+    };
+    if (k0 > 0 && k0 % CH == 0)
+      ids = check_block_ids<TRACE, TB>(P, read_block_ids<TB>(P, bt_row, r.blk_begin, t0, dt, k0, lane), s, r,
+                                       t0, dt, k0, lane);
+    BTile<D, TB> ring[NBUF];
+#pragma unroll
+    for (int j = 0; j < NBUF; ++j) issue(ring[j], k0 + j);
+#pragma unroll
+    for (int j = 0; j < CT; ++j) {
+      const int k = k0 + j;
+      if (k < nk) compute(ring[j % NBUF], t0 + k * dt);
+      if (j + NBUF < CT) issue(ring[j % NBUF], k + NBUF);
     }
   }
 
@@ -837,34 +800,8 @@ __global__ __launch_bounds__(kReduceThreads) void pa_lse_reduce_kernel(ReducePar
 
 
 // ---------------------------------------------------------------- host side
-// Launch shapes of the bf16 partition kernel: waves per workgroup, blocks per
-// tile and register prefetch, per head_dim (compile-time tuning knobs).
-#ifndef PA_BF16_D128_NW
-#define PA_BF16_D128_NW 4
-#endif
-#ifndef PA_BF16_D128_TB
-#define PA_BF16_D128_TB 2
-#endif
-#ifndef PA_BF16_D256_NW
-#define PA_BF16_D256_NW 2
-#endif
-#ifndef PA_V1_D256_NW
-#define PA_V1_D256_NW 4
-#endif
-#ifndef PA_BF16_D256_TB
-#define PA_BF16_D256_TB 1
-#endif
-#ifndef PA_V1_D128_NW
-#define PA_V1_D128_NW 8
-#endif
-#ifndef PA_V1_D128_TB
-#define PA_V1_D128_TB 2
-#endif
-#ifndef PA_PREFETCH
-#define PA_PREFETCH 0
-#endif
 constexpr int kNW = 4;  // waves per f32 partition workgroup
-constexpr int kMaxNW = 16;
+constexpr int kMaxNW = 8;
 
 int partition_size(const pa_shape* sh) { return sh->partition_size ? sh->partition_size : kPart; }
 
@@ -896,63 +833,116 @@ int check_all(const void* out, const void* q, const void* k, const void* v, cons
   return PA_OK;
 }
 
-// Dynamic LDS: [per-wave max | exp-sum] followed by a union of the main
-// loop's scratch (bf16: per-wave K tiles, optional q) and the merge rows
-// [wave][head][D + 4] floats.
+// Dynamic LDS: [per-wave max | exp-sum][merge rows [wave][head][D + 4]
+// floats], followed (16-bit caches) by the per-wave K tiles.
 size_t merge_bytes(int nw, int D, int G) {
   return ((size_t)2 * nw * 16 + (size_t)nw * G * (D + 4)) * sizeof(float);
 }
 
-template <typename T, int D, int NW, int TB>
-hipError_t launch_h16(const Params& P, bool trace, dim3 grid, const Launch& L) {
-  constexpr bool QLDS = (D == 128) ? PA_D128_Q_LDS : PA_D256_Q_LDS;
-  const size_t head = (size_t)2 * NW * 16 * sizeof(float);
-  const size_t qarea = QLDS ? (size_t)(D / 32) * 64 * 16 : 0;
-  const size_t ktiles = (size_t)NW * TB * 16 * D * sizeof(T);
-  const size_t smem = head + std::max(qarea + ktiles, merge_bytes(NW, D, P.G) - head);
-  auto kern = trace ? pa_partition_h16<T, D, NW, TB, PA_PREFETCH, true>
-                    : pa_partition_h16<T, D, NW, TB, PA_PREFETCH, false>;
+// Launch with `smem` bytes of dynamic LDS. Above the default 64 KB a kernel
+// needs its limit raised; that is done once per kernel and device, to the
+// most any call of that kernel can ask for, not on every launch.
+template <void (*kern)(Params)>
+hipError_t launch_lds(size_t max_smem, dim3 grid, dim3 block, size_t smem, const Launch& L, const Params& P) {
   if (smem > 65536) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
-    if (e != hipSuccess) return e;
+    static std::atomic<uint64_t> raised{0};  // bit d: done on device d
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0;
+    if (!bit || !(raised.load(std::memory_order_acquire) & bit)) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_smem);
+      if (e != hipSuccess) return e;
+      raised.fetch_or(bit, std::memory_order_release);
+    }
   }
-  return launch(kern, grid, dim3(NW * 64), smem, L, P);
+  return launch(kern, grid, block, smem, L, P);
+}
+
+// One launch shape of the 16-bit partition kernel: NW waves per workgroup,
+// TB blocks per tile, NBUF tiles in flight per wave, CT tiles per unrolled
+// chunk, WPE waves per SIMD.
+template <int NW_, int TB_, int NBUF_, int CT_, int WPE_>
+struct Shape16 {
+  static constexpr int NW = NW_, TB = TB_, NBUF = NBUF_, CT = CT_, WPE = WPE_;
+};
+
+template <typename T, int D, typename S>
+hipError_t launch_h16(const Params& P, bool trace, dim3 grid, const Launch& L) {
+  const size_t ktiles = (size_t)S::NW * S::TB * 16 * D * sizeof(T);
+  const size_t smem = merge_bytes(S::NW, D, P.G) + ktiles;
+  const size_t max_smem = merge_bytes(S::NW, D, 16) + ktiles;
+  if (trace)
+    return launch_lds<pa_partition_h16<T, D, S::NW, S::TB, S::NBUF, S::CT, S::WPE, true>>(max_smem, grid, dim3(S::NW * 64),
+                                                                                    smem, L, P);
+  return launch_lds<pa_partition_h16<T, D, S::NW, S::TB, S::NBUF, S::CT, S::WPE, false>>(max_smem, grid, dim3(S::NW * 64),
+                                                                                   smem, L, P);
 }
 
 template <int D>
 hipError_t launch_f32(const Params& P, bool trace, dim3 grid, const Launch& L) {
   const size_t smem = merge_bytes(kNW, D, P.G);
-  auto kern = trace ? pa_partition_f32<D, kNW, true> : pa_partition_f32<D, kNW, false>;
-  return launch(kern, grid, dim3(kNW * 64), smem, L, P);
+  const size_t max_smem = merge_bytes(kNW, D, 16);
+  if (trace) return launch_lds<pa_partition_f32<D, kNW, true>>(max_smem, grid, dim3(kNW * 64), smem, L, P);
+  return launch_lds<pa_partition_f32<D, kNW, false>>(max_smem, grid, dim3(kNW * 64), smem, L, P);
 }
 
-// Launch shape of the 16-bit kernel at head_dim 128, chosen from sizes alone
-// (no device data is read on the host):
-//   single-pass only (mode V1, or a table no wider than the V1 threshold):
-//     few long workgroups -> 8 waves, two-block tiles;
-//   small grids (<= kSmallGrid workgroups, about 4 per CU): one-block tiles,
-//     whose lower register count keeps 4 waves per SIMD resident;
-//   otherwise 4 waves, two-block tiles.
+// Launch shapes of the 16-bit kernel, chosen from sizes alone (no device
+// data is read on the host).
+//   head_dim 128:
+//     single-pass only (mode V1, or a table no wider than the V1 threshold):
+//       few long workgroups -> 8 waves, two-block tiles;
+//     at most one workgroup per CU: every workgroup streams on a CU of its
+//       own, bound by the CU's load rate, so each wave keeps two one-block
+//       tiles in flight (2 waves per SIMD is all such a grid occupies);
+//     up to kSmallGrid workgroups: one-block tiles, one in flight (with a
+//       deeper ring the first workgroup on a CU takes the CU's load queue
+//       and the second one starts late: 100K tokens, 392 workgroups, 20.9
+//       against 21.8-22.2 us);
+//     otherwise (batches) one-block tiles, two in flight, 3 waves per SIMD:
+//       on 64 mixed sequences the long single-pass items stream faster with
+//       two tiles in flight (partition kernel 180 against 197 us with
+//       two-block tiles and one in flight).
+//   head_dim 256: single-pass only -> 4 waves; otherwise 2 waves (more
+//     independent workgroups per CU; on 256 sequences of 1K-32K tokens 2.8%
+//     faster than 4 waves, which stream one long context faster).
+using ShapeV1D128 = Shape16<8, 2, 1, 8, 3>;
+using ShapeRingD128 = Shape16<4, 1, 2, 8, 2>;
+using ShapeSmallD128 = Shape16<4, 1, 1, 8, 3>;
+using ShapeD128 = Shape16<4, 1, 2, 8, 3>;
+using ShapeV1D256 = Shape16<4, 1, 1, 8, 2>;
+using ShapeD256 = Shape16<2, 1, 1, 16, 2>;
 constexpr int64_t kSmallGrid = 1024;
+
+// Compute units of the current device (queried once per device).
+int64_t device_cus() {
+  static std::atomic<int> cus[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  int n = cus[dev].load(std::memory_order_relaxed);
+  if (n <= 0) {
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cus[dev].store(n, std::memory_order_relaxed);
+  }
+  return n;
+}
+
+bool single_pass_grid(const Params& P) {
+  return P.mode == PA_MODE_V1 || (P.mode == PA_MODE_AUTO && (int64_t)P.MB * kBS <= kThresh);
+}
 
 template <typename T>
 hipError_t launch_h16_d128(const Params& P, bool trace, dim3 grid, const Launch& L) {
-  const bool single_pass = P.mode == PA_MODE_V1 || (P.mode == PA_MODE_AUTO && (int64_t)P.MB * kBS <= kThresh);
-  if (single_pass) return launch_h16<T, 128, PA_V1_D128_NW, PA_V1_D128_TB>(P, trace, grid, L);
-  if ((int64_t)grid.x <= kSmallGrid) return launch_h16<T, 128, 4, 1>(P, trace, grid, L);
-  return launch_h16<T, 128, PA_BF16_D128_NW, PA_BF16_D128_TB>(P, trace, grid, L);
+  if (single_pass_grid(P)) return launch_h16<T, 128, ShapeV1D128>(P, trace, grid, L);
+  if ((int64_t)grid.x <= device_cus()) return launch_h16<T, 128, ShapeRingD128>(P, trace, grid, L);
+  if ((int64_t)grid.x <= kSmallGrid) return launch_h16<T, 128, ShapeSmallD128>(P, trace, grid, L);
+  return launch_h16<T, 128, ShapeD128>(P, trace, grid, L);
 }
 
-// Launch shape at head_dim 256: grids with partitioned sequences run 2-wave
-// workgroups (more independent workgroups per CU; on 256 sequences of 1K-32K
-// tokens 2.8% faster than 4 waves), single-pass-only grids keep 4 waves, which
-// stream one long context faster.
 template <typename T>
 hipError_t launch_h16_d256(const Params& P, bool trace, dim3 grid, const Launch& L) {
-  const bool single_pass = P.mode == PA_MODE_V1 || (P.mode == PA_MODE_AUTO && (int64_t)P.MB * kBS <= kThresh);
-  if (single_pass) return launch_h16<T, 256, PA_V1_D256_NW, PA_BF16_D256_TB>(P, trace, grid, L);
-  return launch_h16<T, 256, PA_BF16_D256_NW, PA_BF16_D256_TB>(P, trace, grid, L);
+  if (single_pass_grid(P)) return launch_h16<T, 256, ShapeV1D256>(P, trace, grid, L);
+  return launch_h16<T, 256, ShapeD256>(P, trace, grid, L);
 }
 
 hipError_t launch_partitions(const Params& P, int D, int dtype, bool trace, const Launch& stream) {
@@ -978,10 +968,7 @@ constexpr int64_t kReduceMinWGs = 2048;
 // Partial sets up to this size (tmp_out bytes) are reduced with speculative
 // first loads: the kernel is then latency-bound and the loads it may waste
 // (partitions past a short sequence's end) are few.
-#ifndef PA_REDUCE_SPEC_BYTES
-#define PA_REDUCE_SPEC_BYTES (8 << 20)
-#endif
-constexpr int64_t kReduceSpecBytes = PA_REDUCE_SPEC_BYTES;
+constexpr int64_t kReduceSpecBytes = 8 << 20;
 
 template <typename T, int CW>
 hipError_t launch_reduce_cw(bool spec, dim3 grid, dim3 block, const Launch& L, const ReduceParams& R) {

@@ -38,15 +38,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? lo : (v > hi ? hi : v); }
 
-#ifndef PA_MOE_NT
-#define PA_MOE_NT 1
-#endif
 // Rows read once carry the non-temporal hint: with four 1 KB slices per
 // combine pass, measured 117.7 -> 104.4 us for the combine at 16384 tokens x
 // top 8 x 2048 bf16. Stores stay plain: non-temporal stores made the
 // permute's scattered row writes slower (126 against 90 us, same workload).
 __device__ __forceinline__ u32x4 ld_rows(const void* p) {
-  if constexpr (PA_MOE_NT) return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
   return *reinterpret_cast<const u32x4*>(p);
 }
 
@@ -366,10 +363,7 @@ __global__ __launch_bounds__(kSortChunk) void moe_sort_scatter_kernel(const int3
 // the same per-chunk ranks, chunk after chunk, with each expert's running
 // count of the earlier chunks kept in LDS; then the offsets scan and the
 // scatter. Same result as the four-launch path.
-#ifndef PA_MOE_SORT_SMALL_CHUNKS
-#define PA_MOE_SORT_SMALL_CHUNKS 4
-#endif
-constexpr int kSortSmallChunks = PA_MOE_SORT_SMALL_CHUNKS;
+constexpr int kSortSmallChunks = 4;
 static_assert(kSortSmallChunks <= 8, "the single-workgroup sort is instantiated for up to 8 chunks");
 
 template <int R>
@@ -518,10 +512,7 @@ struct Row16<_Float16> : Row16Half<_Float16> {};
 // issues the loads of up to 8 choices for all of them before any arithmetic,
 // so a wave keeps 16 loads of 16 bytes in flight; the sum still runs in the
 // order j = 0..K-1 for every element.
-#ifndef PA_COMBINE_U
-#define PA_COMBINE_U 4
-#endif
-constexpr int kCombineU = PA_COMBINE_U;
+constexpr int kCombineU = 4;
 
 template <typename E>
 __global__ __launch_bounds__(kThreads) void moe_combine_kernel(char* __restrict__ out, const char* __restrict__ y,

@@ -40,9 +40,6 @@ namespace {
 // builtin for these swaps returned the first result in place of the second
 // when both inputs held the same value. The s_nop pairs cover the VALU ->
 // lane-swap -> VALU data hazards.
-#ifndef PA_PREFILL_PERMLANE
-#define PA_PREFILL_PERMLANE 1
-#endif
 template <bool SUM>
 __device__ __forceinline__ float rows_reduce(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
@@ -55,14 +52,8 @@ __device__ __forceinline__ float rows_reduce(float x) {
   const float b0 = __builtin_bit_cast(float, a), b1 = __builtin_bit_cast(float, b);
   return SUM ? b0 + b1 : fmaxf(b0, b1);
 }
-__device__ __forceinline__ float rows_max(float x) {
-  if constexpr (PA_PREFILL_PERMLANE) return rows_reduce<false>(x);
-  return group_max(x);
-}
-__device__ __forceinline__ float rows_sum(float x) {
-  if constexpr (PA_PREFILL_PERMLANE) return rows_reduce<true>(x);
-  return group_sum(x);
-}
+__device__ __forceinline__ float rows_max(float x) { return rows_reduce<false>(x); }
+__device__ __forceinline__ float rows_sum(float x) { return rows_reduce<true>(x); }
 
 // gfx950 LDS transpose read of 16-bit data. Within each group of 16 lanes,
 // lane j reads 4 consecutive elements in[j][0..3] at its own address; lane i

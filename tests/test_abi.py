@@ -230,3 +230,33 @@ def test_load_binds_to_one_hip_runtime():
     res = subprocess.run([sys.executable, "-c", code], cwd=root, capture_output=True, text=True, timeout=300)
     assert res.returncode == 0, res.stderr
     assert res.stdout.strip().splitlines()[-1] == "1"
+
+
+def test_binding_checks_buffer_sizes_before_launch():
+    """The binding compares every decode buffer with the shape it passes, on
+    the host: partials allocated for 512-token partitions and a call that
+    opts into 256-token ones (twice the partitions) raise instead of letting
+    the kernel write past tmp_out's end."""
+    import torch
+    S, H, Hkv, D, MB = 2, 16, 2, 128, 100
+    sh512 = shape(num_seqs=S, max_blocks_per_seq=MB)
+    sh256 = shape(num_seqs=S, max_blocks_per_seq=MB, partition_size=256)
+    P512 = (MB * 16 + 511) // 512
+    es = torch.empty((S, H, P512))
+    ml = torch.empty((S, H, P512))
+    to = torch.empty((S, H, P512, D))
+    out = torch.empty((S, H, D))
+    sl = torch.zeros(S, dtype=torch.int32)
+    L.check_sizes(sh512, out=out, seq_lens=sl, partials=(es, ml, to))          # consistent: no error
+    with pytest.raises(L.PaError, match="tmp_out|exp_sums") as e:
+        L.check_sizes(sh256, out=out, seq_lens=sl, partials=(es, ml, to))
+    assert e.value.status == L.PA_EINVAL
+    with pytest.raises(L.PaError, match="seq_lens"):
+        L.check_sizes(sh512, out=out, seq_lens=torch.zeros(S + 1, dtype=torch.int32))
+    with pytest.raises(L.PaError, match="out"):
+        L.check_sizes(sh512, out=torch.empty((S, H, D // 2)), seq_lens=sl)
+    with pytest.raises(L.PaError, match="tmp_out"):
+        L.check_sizes(sh512, partials=(es, ml, torch.empty((S, H, P512 - 1, D))))
+    with pytest.raises(L.PaError, match="cache"):
+        L.check_sizes(sh512, k_cache=torch.empty((999, Hkv, 16, D)))
+    L.check_sizes(sh512, k_cache=torch.empty((1000, Hkv, 16, D)))

@@ -56,10 +56,21 @@ def run(x, dev, mode="auto", d=None, ps=0):
 
 
 def ref_rows(x, seqs=None):
-    seqs = range(x.cfg.num_seqs) if seqs is None else seqs
+    """Oracle rows of the given sequences (all by default), one sequence per
+    task on a thread pool sized to the host's cores (the oracle's matrix
+    products release the interpreter lock), each task's BLAS single-threaded."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    seqs = list(range(x.cfg.num_seqs) if seqs is None else seqs)
     lists = oracle.gather_list(x.block_tables, x.seq_lens)
-    return {s: oracle.attend_seq(x.q[s], x.k_cache, x.v_cache, lists[s], int(x.seq_lens[s]), x.scale,
-                                 x.cfg.dtype) for s in seqs}
+    one = lambda s: oracle.attend_seq(x.q[s], x.k_cache, x.v_cache, lists[s], int(x.seq_lens[s]), x.scale,
+                                      x.cfg.dtype)
+    from threadpoolctl import threadpool_limits
+    workers = max(1, min(16, len(os.sched_getaffinity(0)), len(seqs)))
+    # one BLAS thread per task: a pool over multithreaded BLAS oversubscribes
+    # the cores (measured 40x slower on the batch-256 workload)
+    with threadpool_limits(1), ThreadPoolExecutor(workers) as ex:
+        return dict(zip(seqs, ex.map(one, seqs)))
 
 
 def max_err(got, ref):
@@ -76,22 +87,6 @@ def assert_close(x, out, seqs=None, label=""):
     return got
 
 
-def sample_seqs(lens, n, rng):
-    """Shortest, longest, the two nearest the V1/V2 threshold, and random others."""
-    lens = np.asarray(lens)
-    order = np.argsort(lens)
-    pick = {int(order[0]), int(order[-1])}
-    below = np.where(lens <= 8192)[0]
-    above = np.where(lens > 8192)[0]
-    if below.size:
-        pick.add(int(below[np.argmax(lens[below])]))
-    if above.size:
-        pick.add(int(above[np.argmin(lens[above])]))
-    rest = [i for i in range(lens.size) if i not in pick]
-    pick.update(int(i) for i in rng.choice(rest, size=min(n - len(pick), len(rest)), replace=False))
-    return sorted(pick)
-
-
 # ---------------------------------------------------------------- the five workloads
 @pytest.mark.parametrize("num", [1, 2, 3, 4, 5])
 def test_config_parity(dev, num):
@@ -99,11 +94,7 @@ def test_config_parity(dev, num):
     x = W.make_inputs(num)
     say(f"config {num} {x.cfg.name}: S={x.cfg.num_seqs} sum(L)={int(x.seq_lens.sum())} NB={x.num_blocks}; pa_decode")
     out, _ = run(x, dev, "auto")
-    if num <= 4:
-        seqs = None
-    else:
-        seqs = sample_seqs(x.seq_lens, 16, np.random.default_rng(5))
-    got = assert_close(x, out, seqs, "auto")
+    got = assert_close(x, out, None, "auto")   # every output row of every workload
     assert np.isfinite(got).all()
 
 
@@ -151,7 +142,10 @@ def test_v1_and_v2_agree(dev):
 
 @pytest.mark.parametrize("dtype,D,H,Hkv", [("bf16", 128, 32, 2), ("bf16", 256, 4, 4), ("f32", 256, 3, 1),
                                            ("f32", 128, 16, 2), ("bf16", 128, 5, 1), ("f16", 128, 16, 2),
-                                           ("f16", 256, 8, 1)])
+                                           ("f16", 256, 8, 1),
+                                           # group size 16 at head_dim 256: the merge rows need more than
+                                           # the default 64 KB of LDS (fp32 and the 16-bit single pass)
+                                           ("f32", 256, 16, 1), ("bf16", 256, 16, 1), ("bf16", 128, 16, 1)])
 @pytest.mark.parametrize("mode", MODES)
 def test_group_sizes(dev, dtype, D, H, Hkv, mode):
     lens = [3, 600, 9000]
@@ -584,8 +578,7 @@ def test_config_parity_partition_256(dev, num):
     x = W.make_inputs(num)
     say(f"config {num} {x.cfg.name} with 256-token partitions")
     out, _ = run(x, dev, "auto", ps=256)
-    seqs = None if num <= 4 else sample_seqs(x.seq_lens, 12, np.random.default_rng(6))
-    assert np.isfinite(assert_close(x, out, seqs, "auto/256")).all()
+    assert np.isfinite(assert_close(x, out, None, "auto/256")).all()
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])

@@ -89,7 +89,20 @@ def test_prefill_workload_parity(dev, num):
     x = W.make_prefill_inputs(num)
     say(f"prefill workload {num} {x.cfg.name}: tokens={x.num_query_tokens} L={x.seq_lens.tolist()[:8]}")
     out = run(x, dev)
-    n = {1: 10, 2: 24, 3: 24, 4: 24}[num]
+    if num in (2, 4):
+        # every chunk token: the whole-batch oracle fits in memory and seconds
+        ref = oracle.attend_prefill(x.q, x.k_cache, x.v_cache, x.block_tables, x.seq_lens, x.query_start_loc,
+                                    x.scale, x.cfg.dtype)
+        got = W.from_device(out)
+        worst = max_err(got, ref)
+        say(f"  {x.cfg.name}: max|err| = {worst:.3e} over all {x.num_query_tokens} tokens")
+        assert worst <= TOL[x.cfg.dtype]
+        assert np.isfinite(got).all()
+        return
+    # workloads 1 and 3: a chunk of 2048 over 100K tokens, and eight chunks over
+    # up to 32K: the whole-batch fp64 score matrices would not fit, so sampled
+    # rows (the first and last of every chunk and random others)
+    n = {1: 10, 3: 24}[num]
     check_rows(x, out, sample_rows(x, n, np.random.default_rng(num)), x.cfg.name)
 
 
