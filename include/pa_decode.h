@@ -97,7 +97,8 @@ enum {
   PA_EUNSUPPORTED = -2, /* D not 128/256, block_size != 16, G > 16, unknown dtype/mode,
                          partition_size not 0/256/512 */
   PA_EALIGN = -3,       /* a pointer is not 16-byte aligned */
-  PA_EHIP = -4          /* the HIP launch failed */
+  PA_EHIP = -4,         /* the HIP launch failed */
+  PA_ESCRATCH = -5      /* pa_decode_noalloc: the partials do not fit the library's scratch */
 };
 
 #define PA_BLOCK_SIZE 16
@@ -126,6 +127,26 @@ int pa_decode_v2(void* out, const void* q, const void* k_cache, const void* v_ca
 int pa_decode(void* out, const void* q, const void* k_cache, const void* v_cache,
               const int32_t* block_tables, const int32_t* seq_lens, const pa_shape* shape,
               float scale, float* exp_sums, float* max_logits, float* tmp_out, void* stream);
+
+/* pa_decode without caller buffers and without any allocation, for callers
+ * that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc). Same kernels, launch
+ * shapes and results as pa_decode (bitwise); the partials live in one
+ * library-owned device array of PA_NOALLOC_SCRATCH_BYTES per GPU, kept until
+ * the process ends (its address is looked up once per device, on the first
+ * call there).
+ *   Limit: S * H * Pmax * (D + 2) floats (plus alignment) must fit; larger
+ *   shapes return PA_ESCRATCH before anything is launched. 64 MiB holds, at
+ *   16 heads and head_dim 128, the partials of 20 sequences of 100K tokens.
+ *   Nothing in the array needs to start at zero: every partial the reduce
+ *   reads is written earlier in the same call.
+ *   Calls that overlap on one GPU (different streams, or threads without
+ *   ordering) share that array and race; calls ordered on one stream do not.
+ * Arguments, layouts and the other errors as for pa_decode. */
+#define PA_NOALLOC_SCRATCH_BYTES (64u << 20)
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* seq_lens, const pa_shape* shape,
+                      float scale, void* stream);
 
 /* Phase 1 alone under `mode`: single-pass sequences write out, partitioned
  * ones write partials. pa_decode = pa_decode_partitions(AUTO) +

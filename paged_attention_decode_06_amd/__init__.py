@@ -8,7 +8,8 @@ this package is its thin ctypes binding plus the seeded input generators
 """
 from ._lib import (  # noqa: F401
     BLOCK_SIZE, HipEvents, PARTITION_SIZE, V2_THRESHOLD, MODE_AUTO, MODE_V1, MODE_V2, PA_F32, PA_BF16, PA_F16,
-    PaError, PaShape, alloc_partials, load, make_shape, max_partitions, pa_decode, pa_decode_partitions,
+    PaError, PaShape, alloc_partials, load, make_shape, max_partitions, pa_decode, pa_decode_noalloc,
+    pa_decode_partitions,
     pa_decode_partitions_debug, pa_decode_partitions_timed, pa_decode_v1, pa_decode_v2, pa_lse_reduce,
     pa_lse_reduce_timed, pa_prefill, status_string, check_sizes,
     pa_probe_empty, pa_probe_paged_read, probe_read_grid,

@@ -18,7 +18,8 @@ HEADERS = [HEADER, os.path.join(os.path.dirname(HERE), "include", "pa_moe.h"),
 
 PA_F32, PA_BF16, PA_F16 = 0, 1, 2
 MODE_AUTO, MODE_V1, MODE_V2 = 0, 1, 2
-PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EALIGN, PA_EHIP = 0, -1, -2, -3, -4
+PA_OK, PA_EINVAL, PA_EUNSUPPORTED, PA_EALIGN, PA_EHIP, PA_ESCRATCH = 0, -1, -2, -3, -4, -5
+NOALLOC_SCRATCH_BYTES = 64 << 20
 BLOCK_SIZE, PARTITION_SIZE, V2_THRESHOLD = 16, 512, 8192
 
 
@@ -49,6 +50,7 @@ _SIGS = {
     "pa_decode_v1": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_float, _P]),
     "pa_decode_v2": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_float, _P, _P, _P, _P]),
     "pa_decode": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_float, _P, _P, _P, _P]),
+    "pa_decode_noalloc": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_float, _P]),
     "pa_decode_partitions": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_float,
                                             _P, _P, _P, ctypes.c_int, _P]),
     "pa_lse_reduce": (ctypes.c_int, [_P, _P, _P, _P, _P, ctypes.POINTER(PaShape), ctypes.c_int, _P]),
@@ -275,6 +277,18 @@ def pa_decode(out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums,
               stream=None, partition_size=0):
     _full("pa_decode", out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits,
           tmp_out, stream, partition_size)
+
+
+def pa_decode_noalloc(out, q, k_cache, v_cache, block_tables, seq_lens, scale, stream=None):
+    """pa_decode with the partials in the library's own device scratch: no
+    buffer is allocated, here or in the library (PaError PA_ESCRATCH when a
+    shape's partials exceed it). Calls that overlap on one GPU race."""
+    _check_tensors(out, q, k_cache, v_cache, block_tables, seq_lens)
+    sh = make_shape(q, k_cache, block_tables)
+    check_sizes(sh, out=out, seq_lens=seq_lens, q=q, k_cache=k_cache)
+    _call("pa_decode_noalloc", load().pa_decode_noalloc(_ptr(out), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                                        _ptr(block_tables), _ptr(seq_lens), ctypes.byref(sh),
+                                                        float(scale), _stream(stream, q.device)))
 
 
 def pa_decode_partitions(out, q, k_cache, v_cache, block_tables, seq_lens, scale, exp_sums, max_logits,

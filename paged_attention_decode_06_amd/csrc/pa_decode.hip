@@ -35,6 +35,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "pa_common.h"
 
@@ -1075,7 +1076,63 @@ int run_full(void* out, const void* q, const void* k, const void* v, const int32
 
 }  // namespace
 
+// Partials of pa_decode_noalloc: one array per GPU, owned by the library for
+// the life of the process. Host code never names it directly (in host code
+// the name is a stand-in, not a device address): scratch_base() returns its
+// address on the current device.
+static __device__ __align__(256) float scratch[PA_NOALLOC_SCRATCH_BYTES / sizeof(float)];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up once per
+// device (hipGetSymbolAddress with that device current) and kept; nullptr if
+// the lookup fails.
+float* scratch_base() {
+  static std::mutex mu;
+  static float* base[kMaxDevices] = {};
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!base[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    base[dev] = static_cast<float*>(p);
+  }
+  return base[dev];
+}
+
+// Offsets (floats) of exp_sums, max_logits and tmp_out in the scratch array
+// for a shape, each 256-byte aligned; false when they do not fit.
+bool scratch_layout(const pa_shape* sh, int64_t& off_ml, int64_t& off_to) {
+  const int64_t n = (int64_t)sh->num_seqs * sh->num_heads * max_partitions(sh);
+  const int64_t a = (n + 63) / 64 * 64;
+  off_ml = a;
+  off_to = 2 * a;
+  return off_to + n * sh->head_dim <= (int64_t)(PA_NOALLOC_SCRATCH_BYTES / sizeof(float));
+}
+
+}  // namespace
+
 extern "C" {
+
+int pa_decode_noalloc(void* out, const void* q, const void* k_cache, const void* v_cache,
+                      const int32_t* block_tables, const int32_t* seq_lens, const pa_shape* shape,
+                      float scale, void* stream) {
+  // validate as pa_decode does, except for the partials (the library's own,
+  // aligned), then check that they fit
+  const int st = check_all(out, q, k_cache, v_cache, block_tables, seq_lens, shape, nullptr, nullptr, nullptr,
+                           PA_MODE_AUTO, false, true);
+  if (st != PA_OK) return st;
+  if (shape->num_seqs == 0) return PA_OK;
+  int64_t off_ml = 0, off_to = 0;
+  if (!single_pass_only(shape, PA_MODE_AUTO) && !scratch_layout(shape, off_ml, off_to)) return PA_ESCRATCH;
+  float* base = scratch_base();
+  if (!base) return PA_EHIP;
+  return run_full(out, q, k_cache, v_cache, block_tables, seq_lens, shape, scale, base, base + off_ml,
+                  base + off_to, PA_MODE_AUTO, stream);
+}
 
 int pa_decode_v1(void* out, const void* q, const void* k_cache, const void* v_cache,
                  const int32_t* block_tables, const int32_t* seq_lens, const pa_shape* shape,
@@ -1168,6 +1225,7 @@ const char* pa_status_string(int status) {
     case PA_EUNSUPPORTED: return "unsupported configuration (head_dim, block_size, group size, dtype, mode or size)";
     case PA_EALIGN: return "pointer not aligned (16 bytes for q/caches/out/tmp_out, 4 for int32/f32 arrays)";
     case PA_EHIP: return "HIP kernel launch failed";
+    case PA_ESCRATCH: return "partials larger than the library's scratch (pa_decode_noalloc; use pa_decode)";
     default: return "unknown status";
   }
 }

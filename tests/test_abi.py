@@ -260,3 +260,22 @@ def test_binding_checks_buffer_sizes_before_launch():
     with pytest.raises(L.PaError, match="cache"):
         L.check_sizes(sh512, k_cache=torch.empty((999, Hkv, 16, D)))
     L.check_sizes(sh512, k_cache=torch.empty((1000, Hkv, 16, D)))
+
+
+def test_noalloc_rejects_partials_beyond_its_scratch(lib):
+    """pa_decode_noalloc refuses, before any HIP call, a shape whose partials
+    (S * H * Pmax * (D + 2) floats, each array 256-byte aligned) exceed the
+    library's 64 MiB array; a single-pass-only shape needs no partials."""
+    a = ctypes.c_void_p(A)
+    n = None
+    # 64 sequences x 16 heads x 128 partitions x (128 + 2) floats = 68.2 MB > 64 MiB
+    big = shape(num_seqs=64, max_blocks_per_seq=4096)
+    assert lib.pa_decode_noalloc(a, a, a, a, a, a, ctypes.byref(big), 1.0, n) == L.PA_ESCRATCH
+    assert b"scratch" in lib.pa_status_string(L.PA_ESCRATCH)
+    assert lib.pa_decode_noalloc(a, n, a, a, a, a, ctypes.byref(shape()), 1.0, n) == L.PA_EINVAL
+    assert lib.pa_decode_noalloc(a, a, a, a, a, a, ctypes.byref(shape(head_dim=96)), 1.0, n) == L.PA_EUNSUPPORTED
+    assert lib.pa_decode_noalloc(a, a, a, a, a, a, ctypes.byref(shape(num_seqs=0)), 1.0, n) == L.PA_OK
+    # the arithmetic of the limit at 128 partitions of 16 heads: 63 sequences
+    # fit (130 * 129024 floats), 64 do not
+    assert 2 * 63 * 16 * 128 + 63 * 16 * 128 * 128 <= L.NOALLOC_SCRATCH_BYTES // 4
+    assert 2 * 64 * 16 * 128 + 64 * 16 * 128 * 128 > L.NOALLOC_SCRATCH_BYTES // 4
