@@ -16,11 +16,13 @@
 //   (sequence, KV head, partition) otherwise. Batches map workgroups through
 //   a compact work list built from seq_lens on the device (item_of), with the
 //   long single-pass items first and the unused workgroups at the end. Each
-//   wave walks "tiles" of whole 16-token blocks. For a tile it
-//     - loads K rows so that lane (tok = l%16, grp = l/16) holds 8 consecutive
-//       head dims of token tok: the A operand of a 16x16x32 bf16 MFMA whose M
-//       axis is the 16 tokens and whose N axis is the GQA group (padded to 16),
-//       so one load of K serves every query head of the group;
+//   wave walks "tiles" of whole 16-token blocks, several in flight at a time
+//   where the launch shape asks for it. For a tile it
+//     - loads K as whole rows and transposes it through a swizzled LDS tile
+//       so that lane (tok = l%16, grp = l/16) holds 8 consecutive head dims
+//       of token tok: the A operand of a 16x16x32 bf16 MFMA whose M axis is
+//       the 16 tokens and whose N axis is the GQA group (padded to 16), so
+//       one load of K serves every query head of the group;
 //     - computes S[tok][g] = K q^T, leaving lane l with 4 tokens of head l%16;
 //     - keeps a running max / exp-sum per head (two xor-shuffles per tile);
 //     - computes O^T[d][g] += V^T[d][tok] P[tok][g]: the B operand P is the QK
@@ -36,6 +38,7 @@
 #include <algorithm>
 #include <atomic>
 #include <mutex>
+#include <type_traits>
 
 #include "pa_common.h"
 
@@ -289,9 +292,10 @@ __device__ __forceinline__ void write_zeros(const Params& P, int s, int kvh, int
   for (int e = threadIdx.x * 4; e < P.G * D; e += nthreads * 4) store4<T>(rows, e, z);
 }
 
-// ---------------------------------------------------------------- bf16 path
-// Per wave, tiles of TB whole blocks are streamed through registers with
-// the next tile's loads issued before the current tile's math (PF = 1).
+// ---------------------------------------------------------------- 16-bit path
+// Per wave, tiles of TB whole blocks are streamed through a ring of NBUF
+// register tiles (the launch shapes set TB and NBUF), in straight-line
+// chunks whose loads carry no branch (see the tile loop in the kernel).
 //
 // Loads: both K and V are read as whole rows: lane (g = l%16, grp = l/16)
 // reads 16 bytes at row 4*grp + rr, dims 128h + 8g .. +8, so 16 consecutive
@@ -519,36 +523,40 @@ void pa_partition_h16(Params P) {
   };
 
   // The wave's tiles go in chunks of CT, each chunk straight-line code with
-  // NBUF tiles in flight: tile k's buffer takes the loads of tile k + NBUF
-  // once tile k is computed. A partition is one chunk; a long single pass
-  // takes several, with the ring refilled at the start of each. Tiles past
-  // the item's end load nothing (zero-length resources) and skip the math.
+  // NB tiles in flight: tile k's buffer takes the loads of tile k + NB once
+  // tile k is computed. A partition is one chunk; a long single pass takes
+  // several, with the ring refilled at the start of each. Tiles past the
+  // item's end load nothing (zero-length resources) and skip the math.
   const int nk = t0 < ntiles ? (ntiles - t0 + dt - 1) / dt : 0;  // this wave's tiles
-  for (int k0 = 0; k0 < nk; k0 += CT) {
-    auto issue = [&](BTile<D, TB>& tl, int k) {
-      int64_t phys[TB];
-      bool valid[TB];
-      const int t = t0 + k * dt;
+  auto stream_tiles = [&](auto nb_const) {
+    constexpr int NB = decltype(nb_const)::value;
+    for (int k0 = 0; k0 < nk; k0 += CT) {
+      auto issue = [&](BTile<D, TB>& tl, int k) {
+        int64_t phys[TB];
+        bool valid[TB];
+        const int t = t0 + k * dt;
 #pragma unroll
-      for (int b = 0; b < TB; ++b) {
-        valid[b] = k < nk && r.blk_begin + t * TB + b < r.blk_end;
-        phys[b] = __builtin_amdgcn_readlane(ids, (k % CH) * TB + b);
+        for (int b = 0; b < TB; ++b) {
+          valid[b] = k < nk && r.blk_begin + t * TB + b < r.blk_end;
+          phys[b] = __builtin_amdgcn_readlane(ids, (k % CH) * TB + b);
+        }
+        issue_tile_rsrc<T, D, TB>(tl, kbase, vbase, block_elems, phys, valid, g, grp);
+      };
+      if (k0 > 0 && k0 % CH == 0)
+        ids = check_block_ids<TRACE, TB>(P, read_block_ids<TB>(P, bt_row, r.blk_begin, t0, dt, k0, lane), s, r,
+                                         t0, dt, k0, lane);
+      BTile<D, TB> ring[NB];
+#pragma unroll
+      for (int j = 0; j < NB; ++j) issue(ring[j], k0 + j);
+#pragma unroll
+      for (int j = 0; j < CT; ++j) {
+        const int k = k0 + j;
+        if (k < nk) compute(ring[j % NB], t0 + k * dt);
+        if (j + NB < CT) issue(ring[j % NB], k + NB);
       }
-      issue_tile_rsrc<T, D, TB>(tl, kbase, vbase, block_elems, phys, valid, g, grp);
-    };
-    if (k0 > 0 && k0 % CH == 0)
-      ids = check_block_ids<TRACE, TB>(P, read_block_ids<TB>(P, bt_row, r.blk_begin, t0, dt, k0, lane), s, r,
-                                       t0, dt, k0, lane);
-    BTile<D, TB> ring[NBUF];
-#pragma unroll
-    for (int j = 0; j < NBUF; ++j) issue(ring[j], k0 + j);
-#pragma unroll
-    for (int j = 0; j < CT; ++j) {
-      const int k = k0 + j;
-      if (k < nk) compute(ring[j % NBUF], t0 + k * dt);
-      if (j + NBUF < CT) issue(ring[j % NBUF], k + NBUF);
     }
-  }
+  };
+  stream_tiles(std::integral_constant<int, NBUF>{});
 
   lsum = group_sum(lsum);
   // acc[h*8 + j][i] holds dim 128h + 32*grp + 8i + j.
@@ -681,14 +689,15 @@ __global__ __launch_bounds__(NW * 64) void pa_partition_f32(Params P) {
 // owns float4 t % (CW/4) of the slice and partitions t / (CW/4) + PG*u of
 // each group of PG*NU partitions; all loads of a group are issued at once
 // and folded into the thread's running (max, weight sum, output), rescaled
-// when its max grows; one LDS exchange then merges the per-thread triples.
+// when its max grows. The threads holding the same float4 then merge their
+// triples: first across the lanes of a wave (xor-shuffles), then the waves'
+// results through LDS, in a fixed order (bitwise deterministic).
 // The host picks CW: full rows (one coalesced 1 KB row per wave at D = 256)
 // when there are enough (sequence, head) rows to fill the GPU, narrow slices
 // (more workgroups) otherwise.
 // With SPEC (small partial sets, where the kernel is latency-bound) the first
 // group's loads go out before the sequence length arrives, bounded by Pmax,
 // and entries past the sequence's partition count are masked afterwards.
-// Summation order is fixed (bitwise deterministic).
 struct ReduceParams {
   void* out;
   const float* exp_sums;
@@ -698,18 +707,33 @@ struct ReduceParams {
   int S, H, MB, Pmax, mode, D, PS;
 };
 
+// Merge (M, c, acc) with another triple of the same slice position: both are
+// rescaled to the larger max (natural-log units); an empty triple has M = -inf.
+__device__ __forceinline__ void merge_triple(float& M, float& c, f32x4& acc, float Mo, float co, f32x4 ao) {
+  const float Mn = fmaxf(M, Mo);
+  if (Mn == -INFINITY) return;
+  const float fa = (M > -INFINITY) ? fast_exp2((M - Mn) * kLog2e) : 0.f;
+  const float fb = (Mo > -INFINITY) ? fast_exp2((Mo - Mn) * kLog2e) : 0.f;
+  acc = acc * fa + ao * fb;
+  c = c * fa + co * fb;
+  M = Mn;
+}
+
 template <typename T, int CW, bool SPEC>
 __global__ __launch_bounds__(kReduceThreads) void pa_lse_reduce_kernel(ReduceParams R) {
   constexpr int F4 = CW / 4;                 // float4 per slice
   constexpr int PG = kReduceThreads / F4;    // partition groups
   constexpr int NU = 16;                     // partitions per thread per group
-  __shared__ float sm_m[PG], sm_c[PG];
-  __shared__ f32x4 part[kReduceThreads];
+  constexpr int NWV = kReduceThreads / 64;   // waves
+  static_assert(F4 <= 64 && 64 % F4 == 0, "slice width");
+  __shared__ float sm_m[NWV][F4], sm_c[NWV][F4];
+  __shared__ f32x4 sm_a[NWV][F4];
   const int nchunk = R.D / CW;
   const int dc = blockIdx.x % nchunk;
   const int sh = blockIdx.x / nchunk;
   const int s = sh / R.H;
   const int t = threadIdx.x;
+  const int lane = t & 63, wv = t >> 6;
   const float* ml = R.max_logits + (int64_t)sh * R.Pmax;
   const float* es = R.exp_sums + (int64_t)sh * R.Pmax;
   const float* to = R.tmp_out + (int64_t)sh * R.Pmax * R.D + dc * CW;
@@ -738,10 +762,8 @@ __global__ __launch_bounds__(kReduceThreads) void pa_lse_reduce_kernel(ReducePar
   if (R.mode == PA_MODE_AUTO && L <= kThresh) return;
   const int np = (L + R.PS - 1) / R.PS;
 
-  // Each thread keeps a running (max, weight sum, weighted output) over its
-  // own partitions, rescaled when its max grows; the workgroup then merges
-  // the PG per-group triples once, through LDS (threads of one group hold the
-  // same partitions, so their maxima and sums agree).
+  // The thread's running (max, weight sum, weighted output) over its own
+  // partitions, rescaled when its max grows.
   float M = -INFINITY, ctot = 0.f;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   for (int base = 0; base < np; base += PG * NU) {
@@ -774,28 +796,30 @@ __global__ __launch_bounds__(kReduceThreads) void pa_lse_reduce_kernel(ReducePar
       }
     }
   }
-  if (f4 == 0) {
-    sm_m[pg] = M;
-    sm_c[pg] = ctot;
+  // Merge the triples of one slice position: lanes f4, f4 + F4, ... of a wave
+  // by xor-shuffles, then the waves through LDS.
+#pragma unroll
+  for (int o = F4; o < 64; o <<= 1) {
+    f32x4 ao;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ao[i] = __shfl_xor(acc[i], o);
+    merge_triple(M, ctot, acc, __shfl_xor(M, o), __shfl_xor(ctot, o), ao);
   }
-  part[t] = acc;
+  if (lane < F4) {
+    sm_m[wv][lane] = M;
+    sm_c[wv][lane] = ctot;
+    sm_a[wv][lane] = acc;
+  }
   __syncthreads();
   if (t < F4) {
-    float Mx = -INFINITY;
-#pragma unroll 8
-    for (int g2 = 0; g2 < PG; ++g2) Mx = fmaxf(Mx, sm_m[g2]);
-    float tot = 0.f;
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int g2 = 0; g2 < PG; ++g2) {
-      const float mg = sm_m[g2];
-      const float w = (mg > -INFINITY) ? fast_exp2((mg - Mx) * kLog2e) : 0.f;
-      tot += w * sm_c[g2];
-      sum += w * part[g2 * F4 + t];
-    }
-    const float inv = (tot > 0.f) ? 1.f / tot : 0.f;
+    M = sm_m[0][t];
+    ctot = sm_c[0][t];
+    acc = sm_a[0][t];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) merge_triple(M, ctot, acc, sm_m[w][t], sm_c[w][t], sm_a[w][t]);
+    const float inv = (ctot > 0.f) ? 1.f / ctot : 0.f;
     T* row = reinterpret_cast<T*>(R.out) + (int64_t)sh * R.D + dc * CW;
-    store4<T>(row, 4 * t, sum * inv);
+    store4<T>(row, 4 * t, acc * inv);
   }
 }
 
