@@ -2,6 +2,8 @@
 // the kernel and its C ABI entry point (pa_prefill, declared in pa_decode.h).
 
 #include <algorithm>
+#include <type_traits>
+#include <utility>
 
 #include "pa_common.h"
 
@@ -23,37 +25,32 @@ namespace {
 // waves owns NTW N-tiles of 16 rows and walks every key tile itself (no merge
 // across waves). In the shared form (head_dim 128) the workgroup stages each
 // K/V tile once into one of two LDS buffers (K XOR-swizzled by row so the
-// token-wise operand reads hit distinct banks), with the loads of the next
-// SHD tiles already in flight in registers; every wave reads its operands
-// there. In the per-wave form (head_dim 256) each wave loads its own tile and
-// passes K through a wave-private swizzled LDS tile. V is transposed in
-// registers; P is the QK accumulator rounded to the 16-bit type. Outputs are
-// stored straight from the accumulators (8 consecutive dims per 16-byte
-// store).
-// Max and sum over the four lane groups (lanes l, l^16, l^32, l^48: the same
-// row) with the gfx950 lane-swap moves instead of LDS-routed shuffles.
+// token-wise operand reads hit distinct banks, V read back transposed), with
+// the loads of the next SHD tiles already in flight in registers; every wave
+// reads its operands there. In the per-wave form (head_dim 256) each wave
+// loads its own tile, passes K through a wave-private swizzled LDS tile and
+// transposes V in registers. P is the QK accumulator rounded to the 16-bit
+// type; its row sums come from one more MFMA against a ones operand. Outputs
+// are stored straight from the accumulators.
+// Max over the four lane groups (lanes l, l^16, l^32, l^48: the same row)
+// with the gfx950 lane-swap moves instead of LDS-routed shuffles.
 // v_permlane16_swap a, b exchanges rows 1/3 of a with rows 0/2 of b; with b a
 // copy of a, lane l then holds v[l] and v[l^16] across a and b, and
-// v_permlane32_swap pairs l with l^32 the same way. The max (or the sum, which
-// is commutative) of a and b is then the same value in both lanes of a pair.
+// v_permlane32_swap pairs l with l^32 the same way. The max of a and b is
+// then the same value in both lanes of a pair.
 // Written as inline assembly with both registers read-write: the compiler's
 // builtin for these swaps returned the first result in place of the second
 // when both inputs held the same value. The s_nop pairs cover the VALU ->
 // lane-swap -> VALU data hazards.
-template <bool SUM>
-__device__ __forceinline__ float rows_reduce(float x) {
+__device__ __forceinline__ float rows_max(float x) {
   uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
   asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-  const float a0 = __builtin_bit_cast(float, a), a1 = __builtin_bit_cast(float, b);
-  x = SUM ? a0 + a1 : fmaxf(a0, a1);
+  x = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
   a = __builtin_bit_cast(uint32_t, x);
   b = a;
   asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-  const float b0 = __builtin_bit_cast(float, a), b1 = __builtin_bit_cast(float, b);
-  return SUM ? b0 + b1 : fmaxf(b0, b1);
+  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
 }
-__device__ __forceinline__ float rows_max(float x) { return rows_reduce<false>(x); }
-__device__ __forceinline__ float rows_sum(float x) { return rows_reduce<true>(x); }
 
 // gfx950 LDS transpose read of 16-bit data. Within each group of 16 lanes,
 // lane j reads 4 consecutive elements in[j][0..3] at its own address; lane i
@@ -63,6 +60,16 @@ __device__ __forceinline__ float rows_sum(float x) { return rows_reduce<true>(x)
 // (row = lane % 16, four consecutive k) read straight from row-major data.
 __device__ __forceinline__ i16x4 lds_read_tr16(const void* p) {
   return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(const_cast<void*>(p)));
+}
+
+// Calls f(std::integral_constant<int, i>{}) for i = 0 .. N-1, in order.
+template <typename F, int... I>
+__device__ __forceinline__ void unrolled_impl(F& f, std::integer_sequence<int, I...>) {
+  (f(std::integral_constant<int, I>{}), ...);
+}
+template <int N, typename F>
+__device__ __forceinline__ void unrolled(F& f) {
+  unrolled_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 struct PrefillParams {
@@ -93,7 +100,14 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   const int g = lane & 15, grp = lane >> 4;
 
   const int pairs = P.S * P.Hkv;
-  const int pair = blockIdx.x % pairs, qt = blockIdx.x / pairs;
+  // Launch order: round r = blockIdx / pairs takes query tile nq - 1 - r of
+  // every (sequence, KV head) pair, so the later tiles of each chunk, which
+  // see the most keys, start first and the short ones fill the tail. Within
+  // a round the pairs are rotated by r: workgroups go to the XCDs round-robin,
+  // and without the rotation each XCD would take the same few pairs in every
+  // round (all the tiles of the longest sequences on one XCD).
+  const int nq = (int)(gridDim.x / pairs), r = (int)(blockIdx.x / pairs);
+  const int pair = ((int)(blockIdx.x % pairs) + r) % pairs, qt = nq - 1 - r;
   const int s = pair / P.Hkv, kvh = pair % P.Hkv;
   // Extents, clamped so that no data value can send a read out of bounds.
   int qb = P.qsl[s], qe = P.qsl[s + 1];
@@ -143,6 +157,11 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   }
 
   // B operands of the QK MFMA: lane holds q[row][kk*32 + 8*grp .. +8].
+  // A negative scale is folded into q (an exact sign flip), so that the
+  // softmax below scales by |scale| and takes its running max on the raw
+  // scores (the max commutes with a non-negative scale).
+  const bool neg_scale = P.scale2 < 0.f;
+  const float s2 = fabsf(P.scale2);
   tx8 qv[NTW][KK];
 #pragma unroll
   for (int jj = 0; jj < NTW; ++jj) {
@@ -153,6 +172,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     for (int kk = 0; kk < KK; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (valid[jj]) x = ld16(qrow + kk * 32 + grp * 8);
+      if (neg_scale) x ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
       qv[jj][kk] = __builtin_bit_cast(tx8, x);
     }
   }
@@ -166,15 +186,25 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   const int nblk = (kmax + kBS - 1) / kBS;
   const int ntiles = (nblk + TB - 1) / TB;
 
-  float m[NTW], lsum[NTW];
-  f32x4 acc[NTW][NACC];
+  // Running max (log2 units of the scaled scores), P.V accumulators, and
+  // the row sums of P: one more MFMA per tile multiplies P by a ones
+  // operand, so every lane ends with its row's sum of the same rounded P
+  // that the P.V products used (and the vector ALU adds nothing up).
+  float m[NTW];
+  f32x4 acc[NTW][NACC], accl[NTW];
 #pragma unroll
   for (int jj = 0; jj < NTW; ++jj) {
     m[jj] = -INFINITY;
-    lsum[jj] = 0.f;
+    accl[jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int a = 0; a < NACC; ++a) acc[jj][a] = (f32x4){0.f, 0.f, 0.f, 0.f};
   }
+  tx8 ones8;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones8[i] = (T)1.0f;
+  tx4 ones4;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) ones4[i] = (T)1.0f;
 
   // Physical ids of the next CH tiles: lane j holds block (k * CH * TB + j).
   int ids = 0;
@@ -202,16 +232,82 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     issue_tile<T, D, TB, false>(tl, kbase, vbase, block_elems, phys, vb, g, grp);
   };
 
-  // The math of tile t: K as MFMA A operands (ka); V as raw rows (tl.v,
-  // per-wave form) or as ready V^T A operands (vo, shared form).
+  // The math of tile t in three steps: the QK scores of N-tile jj from K
+  // operands ka; the online-softmax update of that N-tile (running max,
+  // exp-sum, rescale of its accumulators), which hands back P rounded to the
+  // 16-bit type; and P.V. The shared form runs the steps of consecutive
+  // tiles interleaved; the per-wave form runs them in order (compute_ops).
   static_assert(!SH || TB == 2, "the shared form takes two-block tiles");
-  auto compute_ops = [&](tx8 (&ka)[TB][KK], BTile<D, TB>& tl, const auto& vo, int t) {
+  auto qk_scores = [&](const tx8 (&ka)[TB][KK], int jj, f32x4 (&sc)[TB]) {
+#pragma unroll
+    for (int b = 0; b < TB; ++b) {
+      sc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk) sc[b] = H16<T>::mma32(ka[b][kk], qv[jj][kk], sc[b]);
+    }
+  };
+  auto softmax_step = [&](const f32x4 (&sc)[TB], int jj, int t, T (&pb)[TB][4]) {
     const int tok0 = t * TB * kBS;
     const bool full = tok0 + TB * kBS - 1 <= wave_min_pos;  // no row of the wave needs the mask here
-    // V rows at or past kmax (tail slots of the last block, blocks past the
-    // end) are zeroed: a zero weight times NaN would poison the sum. (The
-    // shared form zeroes them on their way into LDS.)
-    if (!SH && tok0 + TB * kBS > kmax) {
+    float mx = -INFINITY;
+    if (full) {
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[b][i]);
+      mx = rows_max(mx);
+      const float mnew = fmaxf(m[jj], mx * s2);  // finite: key 0 is in every row's first tile
+      const float alpha = fast_exp2(m[jj] - mnew);
+      m[jj] = mnew;
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pb[b][i] = (T)fast_exp2(__builtin_fmaf(sc[b][i], s2, -mnew));
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) acc[jj][a] *= alpha;
+        accl[jj] *= alpha;
+      }
+    } else {
+      bool ok[TB][4];
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ok[b][i] = tok0 + b * kBS + 4 * grp + i <= posc[jj];
+          mx = fmaxf(mx, ok[b][i] ? sc[b][i] : -INFINITY);
+        }
+      mx = rows_max(mx);
+      const float mnew = fmaxf(m[jj], mx * s2);  // a row with no key here keeps its max (fmaxf drops NaN)
+      const float alpha = fast_exp2(m[jj] - mnew);
+      m[jj] = mnew;
+#pragma unroll
+      for (int b = 0; b < TB; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pb[b][i] = (T)(ok[b][i] ? fast_exp2(__builtin_fmaf(sc[b][i], s2, -mnew)) : 0.f);
+      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
+#pragma unroll
+        for (int a = 0; a < NACC; ++a) acc[jj][a] *= alpha;
+        accl[jj] *= alpha;
+      }
+    }
+  };
+  auto pack_p2 = [&](const T (&pb)[TB][4]) {  // two-block P as one B operand, in key order 4grp+i, 16+4grp+i
+    tx8 pv;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pv[i] = pb[0][i];
+      pv[4 + i] = pb[TB - 1][i];
+    }
+    return pv;
+  };
+
+  // Per-wave form: P.V from the tile's raw V rows, transposed in registers.
+  // V rows at or past kmax (tail slots of the last block, blocks past the
+  // end) are zeroed first: a zero weight times NaN would poison the sum.
+  auto compute_ops = [&](tx8 (&ka)[TB][KK], BTile<D, TB>& tl, int t) {
+    const int tok0 = t * TB * kBS;
+    if (tok0 + TB * kBS > kmax) {
 #pragma unroll
       for (int b = 0; b < TB; ++b)
 #pragma unroll
@@ -220,72 +316,14 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
 #pragma unroll
             for (int h = 0; h < NH; ++h) tl.v[b][rr][h] = (u32x4){0u, 0u, 0u, 0u};
     }
-
 #pragma unroll
     for (int jj = 0; jj < NTW; ++jj) {
       f32x4 sc[TB];
-#pragma unroll
-      for (int b = 0; b < TB; ++b) {
-        sc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) sc[b] = H16<T>::mma32(ka[b][kk], qv[jj][kk], sc[b]);
-      }
-      float x[TB][4];
-      float mx = -INFINITY;
-      if (full) {
-#pragma unroll
-        for (int b = 0; b < TB; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            x[b][i] = sc[b][i] * P.scale2;
-            mx = fmaxf(mx, x[b][i]);
-          }
-      } else {
-#pragma unroll
-        for (int b = 0; b < TB; ++b)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int kp = tok0 + b * kBS + 4 * grp + i;
-            const float z = (kp <= posc[jj]) ? sc[b][i] * P.scale2 : -INFINITY;
-            x[b][i] = z;
-            mx = fmaxf(mx, z);
-          }
-      }
-      mx = rows_max(mx);
-      const float mnew = fmaxf(m[jj], mx);  // finite: key 0 is in every row's first tile
-      const float alpha = fast_exp2(m[jj] - mnew);
-      m[jj] = mnew;
       T pb[TB][4];
-      float ps = 0.f;
-#pragma unroll
-      for (int b = 0; b < TB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float pe = fast_exp2(x[b][i] - mnew);
-          pb[b][i] = (T)pe;
-          ps += pe;
-        }
-      lsum[jj] = lsum[jj] * alpha + ps;
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-        for (int a = 0; a < NACC; ++a) acc[jj][a] *= alpha;
-      }
-      if constexpr (SH) {
-        tx8 pv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[i] = pb[0][i];
-          pv[4 + i] = pb[1][i];
-        }
-#pragma unroll
-        for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma32(vo[mt], pv, acc[jj][mt]);
-      } else if constexpr (TB == 2) {
-        tx8 pv;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          pv[i] = pb[0][i];
-          pv[4 + i] = pb[1][i];
-        }
+      qk_scores(ka, jj, sc);
+      softmax_step(sc, jj, t, pb);
+      if constexpr (TB == 2) {
+        const tx8 pv = pack_p2(pb);
 #pragma unroll
         for (int h = 0; h < NH; ++h)
 #pragma unroll
@@ -305,6 +343,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
             }
             acc[jj][h * 8 + j] = H16<T>::mma32(__builtin_bit_cast(tx8, a), pv, acc[jj][h * 8 + j]);
           }
+        accl[jj] = H16<T>::mma32(ones8, pv, accl[jj]);
       } else {
         tx4 pv4;
 #pragma unroll
@@ -324,6 +363,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
             }
             acc[jj][h * 8 + j] = H16<T>::mma16(__builtin_bit_cast(tx4, a), pv4, acc[jj][h * 8 + j]);
           }
+        accl[jj] = H16<T>::mma16(ones4, pv4, accl[jj]);
       }
     }
   };
@@ -348,8 +388,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
         const int c16 = 4 * kk + grp;
         ka[b][kk] = __builtin_bit_cast(tx8, ktile[(b * 16 + g) * KCH + (c16 ^ g)]);
       }
-    const tx8 vo_unused[NACC] = {};  // the per-wave form takes V from tl
-    compute_ops(ka, tl, vo_unused, t);
+    compute_ops(ka, tl, t);
   };
 
   if constexpr (SH) {
@@ -366,97 +405,121 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     constexpr int TCH = TB * 16 * KCH;               // 16-byte chunks of K (or V) per tile
     constexpr int PER = 2 * TCH / (NW * 64);         // chunks per thread per tile
     static_assert(PER * NW * 64 == 2 * TCH, "tile chunks must split evenly over the threads");
-    static_assert(SHD % 2 == 0, "stage parity follows the slot index");
     static_assert(KCH == 16, "the K swizzle spans the 16 chunks of a 128-dim row");
     constexpr int RSV = KCH + 2;                     // padded V row stride (chunks)
     constexpr int STGK = TB * 16 * KCH, STGV = TB * 16 * RSV;  // chunks per stage
     u32x4* kst = reinterpret_cast<u32x4*>(smem);     // [2][TB*16][KCH]
     u32x4* vst = kst + 2 * STGK;                     // [2][TB*16][RSV]
-    auto fetch = [&](u32x4 (&stage)[PER], int t) {
-      if (t % CH == 0) refill(t / CH);
-      int64_t phys[TB];
-      bool vb[TB];
-#pragma unroll
-      for (int b = 0; b < TB; ++b) {
-        vb[b] = t * TB + b < nblk;
-        phys[b] = __builtin_amdgcn_readlane(ids, (t % CH) * TB + b);
-      }
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int id = u * NW * 64 + (int)threadIdx.x;
-        const int kv = id / TCH, r = id % TCH;
-        const int b = r / (16 * KCH), row = (r / KCH) % 16, c = r % KCH;
-        int64_t pb = phys[0];
-        bool ok = vb[0];
-#pragma unroll
-        for (int bb = 1; bb < TB; ++bb)
-          if (b == bb) {
-            pb = phys[bb];
-            ok = vb[bb];
-          }
-        if (kv && (t * TB + b) * kBS + row >= kmax) ok = false;
-        const T* src = (kv ? vbase : kbase) + pb * block_elems + row * D + c * 8;
-        stage[u] = ok ? ld16(src) : (u32x4){0u, 0u, 0u, 0u};
-      }
+    // Loads: thread i takes 16-byte chunk (row, c) = ((i / 16) % 16, i % 16)
+    // of block i / 256 of the tile, from K and from V. Its wave's block is
+    // one block-table entry, read by a scalar load one tile ahead; the loads
+    // go through buffer resources that are zero bytes long for blocks past
+    // the end and start past the block for V rows at or past kmax, so those
+    // read as zeros without a branch. Every wave thus issues the same two
+    // vector loads per tile, which keeps the compiler's wait counts exact:
+    // a stage is waited for only when it is deposited, SHD - 1 tiles after
+    // its loads went out.
+    static_assert(PER == 2 && NW * 64 == TB * 16 * KCH, "one K and one V chunk per thread per tile");
+    constexpr uint32_t kBlockBytes = (uint32_t)(kBS * D * sizeof(T));
+    const int tid = (int)threadIdx.x;
+    const int bw = w / (NW / TB);                     // this wave's block within a tile
+    const int lrow = (tid >> 4) & 15, lc = tid & 15;
+    const int loff = (lrow * D + lc * 8) * (int)sizeof(T);
+    u32x4* kdst = kst + (bw * 16 + lrow) * KCH + (lc ^ lrow);
+    u32x4* vdst = vst + (bw * 16 + lrow) * RSV + lc;
+    // The block table through the constant address space: a uniform load
+    // from there is a scalar load, waited for by the barrier's counter
+    // rather than behind the vector loads in flight.
+    const __attribute__((address_space(4))) int32_t* bt_const =
+        (const __attribute__((address_space(4))) int32_t*)(uintptr_t)bt_row;
+    auto block_id = [&](int u) {                      // physical block of this wave's block of tile u
+      const int blk = __builtin_amdgcn_readfirstlane(min(u * TB + bw, nblk - 1));
+      int id = bt_const[blk];
+      if ((uint64_t)(int64_t)id >= (uint64_t)P.NB) id = 0;  // out-of-range ids read block 0
+      return id;
     };
-    auto deposit = [&](const u32x4 (&stage)[PER], int buf) {
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int id = u * NW * 64 + (int)threadIdx.x;
-        const int kv = id / TCH, r = id % TCH;
-        const int b = r / (16 * KCH), row = (r / KCH) % 16, c = r % KCH;
-        if (kv)
-          vst[buf * STGV + (b * 16 + row) * RSV + c] = stage[u];
-        else
-          kst[buf * STGK + (b * 16 + row) * KCH + (c ^ row)] = stage[u];
-      }
+    int id_next = block_id(0);
+    auto fetch = [&](u32x4 (&st)[PER], int u) {
+      const int id = id_next;
+      id_next = block_id(u + 1);
+      const int blk = u * TB + bw;
+      const bool ok = blk < nblk;
+      const int64_t off = ok ? (int64_t)id * block_elems : 0;
+      const uint32_t n = ok ? kBlockBytes : 0u;
+      const __amdgpu_buffer_rsrc_t kr = block_rsrc(kbase + off, n);
+      const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + off, n);
+      st[0] = __builtin_amdgcn_raw_buffer_load_b128(kr, loff, 0, 0);
+      st[1] = __builtin_amdgcn_raw_buffer_load_b128(vr, blk * kBS + lrow < kmax ? loff : (int)kBlockBytes, 0, 0);
     };
     const u32x4* klane[KK];                                                // + b*16*KCH
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) klane[kk] = kst + g * KCH + ((4 * kk + grp) ^ g);
     const char* vlane = reinterpret_cast<const char*>(vst) +
                         ((4 * grp + (g >> 2)) * RSV + ((g >> 1) & 1)) * 16 + (g & 1) * 8;  // + 32 mt
-    // SHD register stages: tile t's slot is t % SHD. At the top of iteration
-    // t that slot is free (tile t went to LDS in iteration t - 1) and takes
-    // the loads of tile t + SHD, which then have SHD tiles of math to arrive
-    // in; after the math, tile t + 1 goes from its slot to the other LDS
-    // stage. The loop runs in groups of SHD so every slot index and stage
-    // parity is a compile-time constant.
-    u32x4 stage[SHD][PER];
-#pragma unroll
-    for (int d = 0; d < SHD; ++d)
-      if (d < ntiles) fetch(stage[d], d);
-    deposit(stage[0], 0);
-    __syncthreads();
-    BTile<D, TB> tl;
-    for (int t0 = 0; t0 < ntiles; t0 += SHD) {
-#pragma unroll
-    for (int d = 0; d < SHD; ++d) {
-      const int t = t0 + d;
-      if (t >= ntiles) break;
-      const int buf = d & 1;  // == t & 1: t0 is a multiple of SHD
-      // slot d held tile t, already in LDS: refill it with tile t + SHD
-      if (t + SHD < ntiles) fetch(stage[d], t + SHD);
+    auto qk_tile = [&](int u, f32x4 (&sc)[NTW][TB]) {  // QK scores of tile u from K slot u & 1
       tx8 ka[TB][KK];
 #pragma unroll
       for (int b = 0; b < TB; ++b)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk)
-          ka[b][kk] = __builtin_bit_cast(tx8, klane[kk][buf * STGK + b * 16 * KCH]);
-      // V^T operand of M-tile mt (head dims 16mt .. 16mt+15): keys
-      // 4grp .. 4grp+3 from block 0 and the same from block 1, in the order
-      // the QK accumulator hands P over.
+        for (int kk = 0; kk < KK; ++kk) ka[b][kk] = __builtin_bit_cast(tx8, klane[kk][(u & 1) * STGK + b * 16 * KCH]);
+#pragma unroll
+      for (int jj = 0; jj < NTW; ++jj) qk_scores(ka, jj, sc[jj]);
+    };
+    // Softmax and P.V of tile u from its scores and V slot u & 1. V^T
+    // operand of M-tile mt (head dims 16mt .. 16mt+15): keys 4grp .. 4grp+3
+    // of block 0 and the same of block 1, in the order the QK accumulator
+    // hands P over.
+    auto pv_tile = [&](int u, const f32x4 (&sc)[NTW][TB]) {
+      const char* vs = vlane + (size_t)(u & 1) * STGV * 16;
       tx8 vo[NACC];
 #pragma unroll
       for (int mt = 0; mt < NACC; ++mt) {
-        const i16x4 lo = lds_read_tr16(vlane + (buf * STGV) * 16 + 32 * mt);
-        const i16x4 hi = lds_read_tr16(vlane + (buf * STGV + 16 * RSV) * 16 + 32 * mt);
+        const i16x4 lo = lds_read_tr16(vs + 32 * mt);
+        const i16x4 hi = lds_read_tr16(vs + 16 * RSV * 16 + 32 * mt);
         vo[mt] = __builtin_bit_cast(tx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
-      compute_ops(ka, tl, vo, t);
-      if (t + 1 < ntiles) deposit(stage[(d + 1) % SHD], buf ^ 1);
-      __syncthreads();
-    }
+#pragma unroll
+      for (int jj = 0; jj < NTW; ++jj) {
+        T pb[TB][4];
+        softmax_step(sc[jj], jj, u, pb);
+        const tx8 pv = pack_p2(pb);
+#pragma unroll
+        for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma32(vo[mt], pv, acc[jj][mt]);
+        accl[jj] = H16<T>::mma32(ones8, pv, accl[jj]);
+      }
+    };
+    // Tile u arrives in register stage u % SHD. Iteration t refills stage
+    // t % SHD (tile t went to LDS in the previous iteration) with tile
+    // t + SHD, runs tile t's QK products, softmax and P.V products from LDS
+    // slot t & 1, moves tile t + 1 from its stage into the other slot, and
+    // ends with one barrier. The loop runs in whole groups of SHD (stage
+    // indices are compile-time); iterations past the last tile only load
+    // nothing and deposit zeros. (Running the next tile's QK products ahead
+    // of this tile's softmax measured no faster.)
+    static_assert(SHD >= 2, "one tile in LDS, at least one more in flight");
+    auto deposit = [&](const u32x4 (&st)[PER], int u) {
+      kdst[(u & 1) * STGK] = st[0];
+      vdst[(u & 1) * STGV] = st[1];
+    };
+    u32x4 stage[SHD][PER];
+#pragma unroll
+    for (int d = 0; d < SHD; ++d) fetch(stage[d], d);
+    deposit(stage[0], 0);
+    __syncthreads();
+    for (int t0 = 0; t0 < ntiles; t0 += SHD) {
+      auto iteration = [&](auto d_const) {
+        constexpr int d = decltype(d_const)::value;
+        const int t = t0 + d;
+        fetch(stage[d], t + SHD);
+        if (t < ntiles) {
+          f32x4 sc[NTW][TB];
+          qk_tile(t, sc);
+          pv_tile(t, sc);
+        }
+        deposit(stage[(d + 1) % SHD], t + 1);
+        __syncthreads();
+      };
+      unrolled<SHD>(iteration);
     }
   } else {
     BTile<D, TB> A;
@@ -473,7 +536,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   // dims). Shared form: acc[jj][mt][i] holds dim 16mt + 4grp + i.
 #pragma unroll
   for (int jj = 0; jj < NTW; ++jj) {
-    const float tot = rows_sum(lsum[jj]);
+    const float tot = accl[jj][0];
     if (!valid[jj]) continue;
     const float inv = live[jj] ? 1.f / tot : 0.f;
     T* orow = out_row(jj);
@@ -501,7 +564,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
 //     few query tiles): 8 waves x 1 N-tile, two-block tiles shared through
 //     LDS, 4 register stages of prefetch;
 //   D = 128, larger grids: 256 rows per workgroup, 8 waves x 2 N-tiles (half
-//     the LDS operand traffic per row), 2 stages;
+//     the LDS operand traffic per row), 2 register stages;
 //   D = 256: 128 rows, 8 waves x 1 N-tile, per-wave one-block tiles (the
 //     register budget of the wider rows).
 constexpr int kPrefillRows = 128;      // rows per workgroup of the smallest shape

@@ -4,6 +4,8 @@ the fp64 oracle (oracle.prefill).
 Tolerances (max |error| over every compared element): 2e-2 for bf16 caches,
 1e-2 for fp16, with fp32 accumulation inside the kernel.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -224,3 +226,26 @@ def test_prefill_large_grid_odd_group(dev):
                               query_lens=rng.integers(150, 201, size=S))
     say(f"prefill large grid, G=3: {x.num_query_tokens} tokens")
     check_all(x, run(x, dev), "large grid G=3")
+
+
+@pytest.mark.parametrize("mult", [-1.0, 0.0, 4.0])
+@pytest.mark.parametrize("D", [128, 256])
+def test_prefill_scale_sign_and_zero(dev, D, mult):
+    """A negative scale (folded into q as a sign flip), a zero scale (every
+    visible key weighs the same) and a large one, on both launch forms."""
+    cfg = W.PrefillConfig(f"scale-d{D}", 2, 16, 2, D, "bf16", ("custom",), ("custom",))
+    x = W.make_prefill_inputs(cfg, seed=61, context_lens=[400, 33], query_lens=[90, 70])
+    x = dataclasses.replace(x, scale=x.scale * mult)
+    say(f"prefill scale x{mult} D={D}")
+    check_all(x, run(x, dev), f"scale x{mult} D={D}")
+
+
+def test_prefill_large_grid_negative_scale(dev):
+    """The 256-row launch shape with a negative scale, every token."""
+    rng = np.random.default_rng(62)
+    S = 40
+    x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=62, context_lens=rng.integers(0, 300, size=S),
+                              query_lens=rng.integers(100, 129, size=S))
+    x = dataclasses.replace(x, scale=-x.scale)
+    say(f"prefill large grid, negative scale: {x.num_query_tokens} tokens")
+    check_all(x, run(x, dev), "large grid, scale < 0")
