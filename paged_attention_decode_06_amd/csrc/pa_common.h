@@ -6,6 +6,8 @@
 // namespace, so every unit gets its own copy.
 #pragma once
 
+#include <atomic>
+
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -240,6 +242,26 @@ hipError_t launch(K kern, dim3 grid, dim3 block, size_t smem, const Launch& L, c
   else
     hipLaunchKernelGGL(kern, grid, block, smem, L.stream, arg);
   return hipGetLastError();
+}
+
+// Launch with `smem` bytes of dynamic LDS. Above the default 64 KB a kernel
+// needs its limit raised; that is done once per kernel and device, to the
+// most any call of that kernel can ask for, not on every launch.
+template <auto kern, typename A>
+hipError_t launch_lds(size_t max_smem, dim3 grid, dim3 block, size_t smem, const Launch& L, const A& P) {
+  if (smem > 65536) {
+    static std::atomic<uint64_t> raised{0};  // bit d: done on device d
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0;
+    if (!bit || !(raised.load(std::memory_order_acquire) & bit)) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_smem);
+      if (e != hipSuccess) return e;
+      raised.fetch_or(bit, std::memory_order_release);
+    }
+  }
+  return launch(kern, grid, block, smem, L, P);
 }
 
 // When there is nothing to launch, a timed call still records its events,

@@ -864,25 +864,6 @@ size_t merge_bytes(int nw, int D, int G) {
   return ((size_t)2 * nw * 16 + (size_t)nw * G * (D + 4)) * sizeof(float);
 }
 
-// Launch with `smem` bytes of dynamic LDS. Above the default 64 KB a kernel
-// needs its limit raised; that is done once per kernel and device, to the
-// most any call of that kernel can ask for, not on every launch.
-template <void (*kern)(Params)>
-hipError_t launch_lds(size_t max_smem, dim3 grid, dim3 block, size_t smem, const Launch& L, const Params& P) {
-  if (smem > 65536) {
-    static std::atomic<uint64_t> raised{0};  // bit d: done on device d
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
-    const uint64_t bit = (dev >= 0 && dev < 64) ? (1ull << dev) : 0;
-    if (!bit || !(raised.load(std::memory_order_acquire) & bit)) {
-      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)max_smem);
-      if (e != hipSuccess) return e;
-      raised.fetch_or(bit, std::memory_order_release);
-    }
-  }
-  return launch(kern, grid, block, smem, L, P);
-}
 
 // One launch shape of the 16-bit partition kernel: NW waves per workgroup,
 // TB blocks per tile, NBUF tiles in flight per wave, CT tiles per unrolled

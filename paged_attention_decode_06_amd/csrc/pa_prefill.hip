@@ -85,7 +85,7 @@ struct PrefillParams {
   float scale2;
 };
 
-template <typename T, int D, int NW, int NTW, int TB, bool SH, int SHD>
+template <typename T, int D, int NW, int NTW, int TB, bool SH, int SHD, int KS>
 __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   typedef typename H16<T>::x8 tx8;
   typedef typename H16<T>::x4 tx4;
@@ -98,6 +98,11 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane & 15, grp = lane >> 4;
+  // Key split: the waves form KS groups of NW / KS; wave w takes row group
+  // w % (NW / KS) and, of every KS consecutive key tiles, tile w / (NW / KS).
+  static_assert(KS == 1 || (SH && NW % KS == 0), "key split: shared form only");
+  constexpr int NWR = NW / KS;  // waves per key group (row groups)
+  const int rg = w % NWR, kg = w / NWR;
 
   const int pairs = P.S * P.Hkv;
   // Launch order: round r = blockIdx / pairs takes query tile nq - 1 - r of
@@ -127,7 +132,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   bool valid[NTW], live[NTW];
 #pragma unroll
   for (int jj = 0; jj < NTW; ++jj) {
-    const int row = (w * NTW + jj) * 16 + g;
+    const int row = (rg * NTW + jj) * 16 + g;
     const int tok = i0 + row / P.G;
     valid[jj] = row < P.QT * P.G && tok < i1;
     tokr[jj] = tok;
@@ -144,7 +149,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   for (int o = 32; o >= 1; o >>= 1) min_pos = min(min_pos, __shfl_xor(min_pos, o));
   const int wave_min_pos = __builtin_amdgcn_readfirstlane(min_pos);
   auto out_row = [&](int jj) -> T* {
-    const int row = (w * NTW + jj) * 16 + g;
+    const int row = (rg * NTW + jj) * 16 + g;
     return reinterpret_cast<T*>(P.out) + ((int64_t)(qb + tokr[jj]) * P.H + kvh * P.G + row % P.G) * D;
   };
 
@@ -165,7 +170,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   tx8 qv[NTW][KK];
 #pragma unroll
   for (int jj = 0; jj < NTW; ++jj) {
-    const int row = (w * NTW + jj) * 16 + g;
+    const int row = (rg * NTW + jj) * 16 + g;
     const T* qrow = reinterpret_cast<const T*>(P.q) +
                     ((int64_t)(qb + tokr[jj]) * P.H + kvh * P.G + row % P.G) * D;
 #pragma unroll
@@ -278,8 +283,11 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
           mx = fmaxf(mx, ok[b][i] ? sc[b][i] : -INFINITY);
         }
       mx = rows_max(mx);
-      const float mnew = fmaxf(m[jj], mx * s2);  // a row with no key here keeps its max (fmaxf drops NaN)
-      const float alpha = fast_exp2(m[jj] - mnew);
+      // A row with no visible key here keeps its max (fmaxf drops the NaN of
+      // -inf * 0); with a key split, a key group's first tile can hide every
+      // key from a row, and then the max stays -inf and alpha must be 1.
+      const float mnew = fmaxf(m[jj], mx * s2);
+      const float alpha = m[jj] == mnew ? 1.f : fast_exp2(m[jj] - mnew);
       m[jj] = mnew;
 #pragma unroll
       for (int b = 0; b < TB; ++b)
@@ -402,24 +410,25 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     // in four LDS cycles of the K reads). V rows at or past kmax go in as
     // zeros. The next tile's chunks are in registers while this
     // tile's math runs; one barrier per tile publishes the next stage.
-    constexpr int TCH = TB * 16 * KCH;               // 16-byte chunks of K (or V) per tile
-    constexpr int PER = 2 * TCH / (NW * 64);         // chunks per thread per tile
-    static_assert(PER * NW * 64 == 2 * TCH, "tile chunks must split evenly over the threads");
     static_assert(KCH == 16, "the K swizzle spans the 16 chunks of a 128-dim row");
+    static_assert(TB == 2 && NW * 64 == TB * 16 * KCH, "per tile, one K and one V chunk per thread");
     constexpr int RSV = KCH + 2;                     // padded V row stride (chunks)
-    constexpr int STGK = TB * 16 * KCH, STGV = TB * 16 * RSV;  // chunks per stage
-    u32x4* kst = reinterpret_cast<u32x4*>(smem);     // [2][TB*16][KCH]
-    u32x4* vst = kst + 2 * STGK;                     // [2][TB*16][RSV]
-    // Loads: thread i takes 16-byte chunk (row, c) = ((i / 16) % 16, i % 16)
-    // of block i / 256 of the tile, from K and from V. Its wave's block is
-    // one block-table entry, read by a scalar load one tile ahead; the loads
-    // go through buffer resources that are zero bytes long for blocks past
-    // the end and start past the block for V rows at or past kmax, so those
-    // read as zeros without a branch. Every wave thus issues the same two
-    // vector loads per tile, which keeps the compiler's wait counts exact:
-    // a stage is waited for only when it is deposited, SHD - 1 tiles after
-    // its loads went out.
-    static_assert(PER == 2 && NW * 64 == TB * 16 * KCH, "one K and one V chunk per thread per tile");
+    constexpr int STGK = TB * 16 * KCH, STGV = TB * 16 * RSV;  // chunks per tile
+    // LDS: two slots (by step parity) of KS tiles each, K [2][KS][TB*16][KCH]
+    // and V [2][KS][TB*16][RSV]. A step is KS consecutive key tiles, one per
+    // key group.
+    u32x4* kst = reinterpret_cast<u32x4*>(smem);
+    u32x4* vst = kst + 2 * KS * STGK;
+    // Loads: for each tile of a step, thread i takes 16-byte chunk
+    // (row, c) = ((i / 16) % 16, i % 16) of block i / 256 of the tile, from K
+    // and from V. Its wave's block is one block-table entry, read by a
+    // scalar load one step ahead; the loads go through buffer resources that
+    // are zero bytes long for blocks past the end and start past the block
+    // for V rows at or past kmax, so those read as zeros without a branch.
+    // Every wave thus issues the same 2 KS vector loads per step, which keeps
+    // the compiler's wait counts exact: a stage is waited for only when it is
+    // deposited, SHD - 1 steps after its loads went out.
+    constexpr int PER = 2 * KS;                      // chunks per thread per step
     constexpr uint32_t kBlockBytes = (uint32_t)(kBS * D * sizeof(T));
     const int tid = (int)threadIdx.x;
     const int bw = w / (NW / TB);                     // this wave's block within a tile
@@ -438,39 +447,53 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
       if ((uint64_t)(int64_t)id >= (uint64_t)P.NB) id = 0;  // out-of-range ids read block 0
       return id;
     };
-    int id_next = block_id(0);
-    auto fetch = [&](u32x4 (&st)[PER], int u) {
-      const int id = id_next;
-      id_next = block_id(u + 1);
-      const int blk = u * TB + bw;
-      const bool ok = blk < nblk;
-      const int64_t off = ok ? (int64_t)id * block_elems : 0;
-      const uint32_t n = ok ? kBlockBytes : 0u;
-      const __amdgpu_buffer_rsrc_t kr = block_rsrc(kbase + off, n);
-      const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + off, n);
-      st[0] = __builtin_amdgcn_raw_buffer_load_b128(kr, loff, 0, 0);
-      st[1] = __builtin_amdgcn_raw_buffer_load_b128(vr, blk * kBS + lrow < kmax ? loff : (int)kBlockBytes, 0, 0);
+    int id_next[KS];
+#pragma unroll
+    for (int j = 0; j < KS; ++j) id_next[j] = block_id(j);
+    auto fetch = [&](u32x4 (&st)[PER], int step) {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const int u = step * KS + j;
+        const int id = id_next[j];
+        id_next[j] = block_id(u + KS);
+        const int blk = u * TB + bw;
+        const bool ok = blk < nblk;
+        const int64_t off = ok ? (int64_t)id * block_elems : 0;
+        const uint32_t n = ok ? kBlockBytes : 0u;
+        const __amdgpu_buffer_rsrc_t kr = block_rsrc(kbase + off, n);
+        const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + off, n);
+        st[2 * j] = __builtin_amdgcn_raw_buffer_load_b128(kr, loff, 0, 0);
+        st[2 * j + 1] =
+            __builtin_amdgcn_raw_buffer_load_b128(vr, blk * kBS + lrow < kmax ? loff : (int)kBlockBytes, 0, 0);
+      }
     };
-    const u32x4* klane[KK];                                                // + b*16*KCH
+    auto deposit = [&](const u32x4 (&st)[PER], int step) {
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        kdst[((step & 1) * KS + j) * STGK] = st[2 * j];
+        vdst[((step & 1) * KS + j) * STGV] = st[2 * j + 1];
+      }
+    };
+    const u32x4* klane[KK];                                                // + tile slot*STGK + b*16*KCH
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) klane[kk] = kst + g * KCH + ((4 * kk + grp) ^ g);
     const char* vlane = reinterpret_cast<const char*>(vst) +
                         ((4 * grp + (g >> 2)) * RSV + ((g >> 1) & 1)) * 16 + (g & 1) * 8;  // + 32 mt
-    auto qk_tile = [&](int u, f32x4 (&sc)[NTW][TB]) {  // QK scores of tile u from K slot u & 1
+    auto qk_tile = [&](int slot, f32x4 (&sc)[NTW][TB]) {  // QK scores of the tile in LDS tile slot `slot`
       tx8 ka[TB][KK];
 #pragma unroll
       for (int b = 0; b < TB; ++b)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) ka[b][kk] = __builtin_bit_cast(tx8, klane[kk][(u & 1) * STGK + b * 16 * KCH]);
+        for (int kk = 0; kk < KK; ++kk) ka[b][kk] = __builtin_bit_cast(tx8, klane[kk][slot * STGK + b * 16 * KCH]);
 #pragma unroll
       for (int jj = 0; jj < NTW; ++jj) qk_scores(ka, jj, sc[jj]);
     };
-    // Softmax and P.V of tile u from its scores and V slot u & 1. V^T
-    // operand of M-tile mt (head dims 16mt .. 16mt+15): keys 4grp .. 4grp+3
-    // of block 0 and the same of block 1, in the order the QK accumulator
-    // hands P over.
-    auto pv_tile = [&](int u, const f32x4 (&sc)[NTW][TB]) {
-      const char* vs = vlane + (size_t)(u & 1) * STGV * 16;
+    // Softmax and P.V of key tile u from its scores and LDS tile slot
+    // `slot`. V^T operand of M-tile mt (head dims 16mt .. 16mt+15): keys
+    // 4grp .. 4grp+3 of block 0 and the same of block 1, in the order the QK
+    // accumulator hands P over.
+    auto pv_tile = [&](int slot, int u, const f32x4 (&sc)[NTW][TB]) {
+      const char* vs = vlane + (size_t)slot * STGV * 16;
       tx8 vo[NACC];
 #pragma unroll
       for (int mt = 0; mt < NACC; ++mt) {
@@ -488,38 +511,74 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
         accl[jj] = H16<T>::mma32(ones8, pv, accl[jj]);
       }
     };
-    // Tile u arrives in register stage u % SHD. Iteration t refills stage
-    // t % SHD (tile t went to LDS in the previous iteration) with tile
-    // t + SHD, runs tile t's QK products, softmax and P.V products from LDS
-    // slot t & 1, moves tile t + 1 from its stage into the other slot, and
-    // ends with one barrier. The loop runs in whole groups of SHD (stage
-    // indices are compile-time); iterations past the last tile only load
-    // nothing and deposit zeros. (Running the next tile's QK products ahead
-    // of this tile's softmax measured no faster.)
-    static_assert(SHD >= 2, "one tile in LDS, at least one more in flight");
-    auto deposit = [&](const u32x4 (&st)[PER], int u) {
-      kdst[(u & 1) * STGK] = st[0];
-      vdst[(u & 1) * STGV] = st[1];
-    };
+    // Step σ arrives in register stage σ % SHD. Iteration σ refills stage
+    // σ % SHD (step σ went to LDS in the previous iteration) with step
+    // σ + SHD, runs the QK products, softmax and P.V products of this wave's
+    // tile σ KS + kg from LDS slot σ & 1, moves step σ + 1 from its stage into
+    // the other slot, and ends with one barrier. The loop runs in whole
+    // groups of SHD (stage indices are compile-time); iterations past the
+    // last step only load nothing and deposit zeros. (Running the next
+    // tile's QK products ahead of this tile's softmax measured no faster.)
+    static_assert(SHD >= 2, "one step in LDS, at least one more in flight");
+    const int nsteps = (ntiles + KS - 1) / KS;
     u32x4 stage[SHD][PER];
 #pragma unroll
     for (int d = 0; d < SHD; ++d) fetch(stage[d], d);
     deposit(stage[0], 0);
     __syncthreads();
-    for (int t0 = 0; t0 < ntiles; t0 += SHD) {
+    for (int s0 = 0; s0 < nsteps; s0 += SHD) {
       auto iteration = [&](auto d_const) {
         constexpr int d = decltype(d_const)::value;
-        const int t = t0 + d;
-        fetch(stage[d], t + SHD);
+        const int step = s0 + d;
+        fetch(stage[d], step + SHD);
+        const int t = step * KS + kg;
         if (t < ntiles) {
           f32x4 sc[NTW][TB];
-          qk_tile(t, sc);
-          pv_tile(t, sc);
+          qk_tile((step & 1) * KS + kg, sc);
+          pv_tile((step & 1) * KS + kg, t, sc);
         }
-        deposit(stage[(d + 1) % SHD], t + 1);
+        deposit(stage[(d + 1) % SHD], step + 1);
         __syncthreads();
       };
       unrolled<SHD>(iteration);
+    }
+    if constexpr (KS > 1) {
+      // Key groups 1 .. KS-1 hand (max, P.V accumulators, row sums) to key
+      // group 0 through LDS (free again after the loop's last barrier), which
+      // rescales each to the common max and adds them up. Records are 16
+      // bytes per lane, lane-major, so the 16-byte accesses hit distinct banks.
+      static_assert(NTW <= 4, "the maxima of a wave's N-tiles share one record");
+      constexpr int REC = NTW * (NACC + 1) + 1;      // 16-byte records per lane
+      f32x4* mrg = reinterpret_cast<f32x4*>(smem);
+      auto at = [&](int k, int e) -> f32x4& { return mrg[(((k - 1) * NWR + rg) * REC + e) * 64 + lane]; };
+      if (kg > 0) {
+        f32x4 mm = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int jj = 0; jj < NTW; ++jj) {
+          mm[jj] = m[jj];
+#pragma unroll
+          for (int a = 0; a < NACC; ++a) at(kg, jj * (NACC + 1) + a) = acc[jj][a];
+          at(kg, jj * (NACC + 1) + NACC) = accl[jj];
+        }
+        at(kg, NTW * (NACC + 1)) = mm;
+      }
+      __syncthreads();
+      if (kg > 0) return;
+#pragma unroll
+      for (int k = 1; k < KS; ++k) {
+        const f32x4 mm = at(k, NTW * (NACC + 1));
+#pragma unroll
+        for (int jj = 0; jj < NTW; ++jj) {
+          // key group 0 saw key 0, so m[jj] is finite; a group without a
+          // visible key has mm = -inf and weighs nothing
+          const float mx = fmaxf(m[jj], mm[jj]);
+          const float f0 = fast_exp2(m[jj] - mx), f1 = fast_exp2(mm[jj] - mx);
+          m[jj] = mx;
+#pragma unroll
+          for (int a = 0; a < NACC; ++a) acc[jj][a] = acc[jj][a] * f0 + at(k, jj * (NACC + 1) + a) * f1;
+          accl[jj] = accl[jj] * f0 + at(k, jj * (NACC + 1) + NACC) * f1;
+        }
+      }
     }
   } else {
     BTile<D, TB> A;
@@ -575,24 +634,25 @@ template <typename T>
 hipError_t launch_prefill_t(PrefillParams P, int D, int maxq, const Launch& L) {
   const int64_t pairs = (int64_t)P.S * P.Hkv;
   auto tiles = [&](int rows) { const int qt = rows / P.G; return pairs * ((maxq + qt - 1) / qt); };
+  constexpr size_t kSlots = (size_t)2 * 2 * 16 * (2 * (128 / 8) + 2) * 16;  // two slots of a K and (padded) V tile
   if (D == 128) {
     if (tiles(128) <= kPrefillSmallGrid) {
-      constexpr int NW = 8, NTW = 1, TB = 2;
+      constexpr int NW = 8, NTW = 2, TB = 2, KS = 2;
       P.QT = 128 / P.G;
-      const size_t smem = (size_t)2 * TB * 16 * (2 * (128 / 8) + 2) * 16;  // two stages of K and (padded) V
-      return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true, 4>, dim3((unsigned)tiles(128)), dim3(NW * 64), smem,
-                    L, P);
+      const size_t merge = (size_t)(KS - 1) * (NW / KS) * (NTW * (8 + 1) + 1) * 64 * 16;
+      const size_t smem = std::max((size_t)KS * kSlots, merge);
+      return launch_lds<pa_prefill_h16<T, 128, NW, NTW, TB, true, 2, KS>>(smem, dim3((unsigned)tiles(128)),
+                                                                           dim3(NW * 64), smem, L, P);
     }
     constexpr int NW = 8, NTW = 2, TB = 2;
     P.QT = 256 / P.G;
-    const size_t smem = (size_t)2 * TB * 16 * (2 * (128 / 8) + 2) * 16;
-    return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true, 2>, dim3((unsigned)tiles(256)), dim3(NW * 64), smem, L,
-                  P);
+    return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true, 2, 1>, dim3((unsigned)tiles(256)), dim3(NW * 64), kSlots,
+                  L, P);
   }
   constexpr int NW = 8, NTW = 1, TB = 1;
   P.QT = 128 / P.G;
   const size_t smem = (size_t)NW * TB * 16 * 256 * sizeof(T);
-  return launch(pa_prefill_h16<T, 256, NW, NTW, TB, false, 1>, dim3((unsigned)tiles(128)), dim3(NW * 64), smem, L,
+  return launch(pa_prefill_h16<T, 256, NW, NTW, TB, false, 1, 1>, dim3((unsigned)tiles(128)), dim3(NW * 64), smem, L,
                 P);
 }
 
