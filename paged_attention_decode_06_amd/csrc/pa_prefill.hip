@@ -72,6 +72,32 @@ __device__ __forceinline__ void unrolled(F& f) {
   unrolled_impl(f, std::make_integer_sequence<int, N>{});
 }
 
+// Runs one step's loads into LDS (fetch) and its math (math) with the LDS
+// slots as restrict pointers: the slot a step loads into is never the slot
+// its math reads. Inlined, the restrict parameters tag every LDS access
+// with alias scopes, which lets the compiler see that the math's reads do
+// not depend on the loads in flight (without them it waits for every
+// outstanding load before each LDS read).
+template <typename Fetch, typename Math>
+__device__ __forceinline__ void with_slots(u32x4* __restrict__ k_next, u32x4* __restrict__ v_next,
+                                           const u32x4* __restrict__ k_cur, const u32x4* __restrict__ v_cur,
+                                           const u32x4* __restrict__ v_prev, Fetch& fetch, Math& math) {
+  fetch(k_next, v_next);
+  math(k_cur, v_cur, v_prev);
+}
+
+// Workgroup barrier for LDS written by loads: waits until at most N loads
+// of this wave are outstanding and its LDS accesses are done, then
+// s_barrier. (A workgroup fence would wait for every load that writes
+// LDS, the ones still prefetching included.) The memory clobber keeps the
+// compiler from moving LDS accesses across it.
+template <int N>
+__device__ __forceinline__ void lds_barrier() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4));  // vmcnt(N) lgkmcnt(0)
+  asm volatile("s_barrier" ::: "memory");
+}
+
 struct PrefillParams {
   const void* q;
   const void* k;
@@ -400,42 +426,45 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   };
 
   if constexpr (SH) {
-    // Shared path: the workgroup loads each K/V tile once, 16 bytes per
-    // thread-chunk, into one of two LDS stages; every wave reads its MFMA
-    // operands there. K rows are XOR-swizzled (chunk c of row r at c ^ r,
-    // as in the per-wave tile); V rows are padded by two 16-byte chunks, so
-    // the four rows a transpose read takes per 16 lanes (8 dwords each) start
-    // 8 dwords apart. Both read patterns measured free of bank conflicts
-    // (padded K rows were not: 17- and 18-chunk strides conflicted on three
-    // in four LDS cycles of the K reads). V rows at or past kmax go in as
-    // zeros. The next tile's chunks are in registers while this
-    // tile's math runs; one barrier per tile publishes the next stage.
-    static_assert(KCH == 16, "the K swizzle spans the 16 chunks of a 128-dim row");
-    static_assert(TB == 2 && NW * 64 == TB * 16 * KCH, "per tile, one K and one V chunk per thread");
-    constexpr int RSV = KCH + 2;                     // padded V row stride (chunks)
-    constexpr int STGK = TB * 16 * KCH, STGV = TB * 16 * RSV;  // chunks per tile
-    // LDS: two slots (by step parity) of KS tiles each, K [2][KS][TB*16][KCH]
-    // and V [2][KS][TB*16][RSV]. A step is KS consecutive key tiles, one per
-    // key group.
+    // Shared path: the workgroup loads each K/V tile once into LDS and every
+    // wave reads its MFMA operands there. The loads go straight from memory
+    // into LDS (buffer loads with the LDS flag: a wave's 64 lanes write 1 KB
+    // at the wave's LDS address, lane L at +16 L), so no registers stage the
+    // tiles and no stores move them. LDS rows are 16 chunks of 16 bytes,
+    // permuted by row so that both operand reads are free of bank conflicts:
+    // K row r keeps chunk c at position c ^ r (the 16 rows a K read takes
+    // hit 16 distinct positions); V row r keeps chunk c at c ^ 2 (r % 8) (the
+    // transpose read takes chunk pairs 2mt, 2mt+1 from rows 4grp .. 4grp+3,
+    // and eight consecutive rows then hit eight distinct 32-byte bank
+    // groups). Each lane loads the global chunk that its LDS position holds.
+    static_assert(KCH == 16, "the permutations span the 16 chunks of a 128-dim row");
+    static_assert(TB == 2 && NW * 64 == TB * 16 * KCH, "per tile, one K and one V chunk per lane");
+    constexpr int TCH = TB * 16 * KCH;               // chunks per K (or V) tile
+    // LDS: NSL slots (step % NSL) of KS tiles each, K [NSL][KS][TB*16][16]
+    // then V [NSL][KS][TB*16][16]. A step is KS consecutive key tiles, one
+    // per key group. Step σ + 2 loads while step σ is computed; with a key
+    // split, key group 1 reads V of step σ - 1 during step σ (below): four
+    // slots cover both, and make every slot index a compile-time constant.
+    constexpr int NSL = 4;
+    constexpr int SHD_ = 2;
+    static_assert(SHD == SHD_, "the shared form prefetches two steps");
     u32x4* kst = reinterpret_cast<u32x4*>(smem);
-    u32x4* vst = kst + 2 * KS * STGK;
-    // Loads: for each tile of a step, thread i takes 16-byte chunk
-    // (row, c) = ((i / 16) % 16, i % 16) of block i / 256 of the tile, from K
-    // and from V. Its wave's block is one block-table entry, read by a
-    // scalar load one step ahead; the loads go through buffer resources that
-    // are zero bytes long for blocks past the end and start past the block
-    // for V rows at or past kmax, so those read as zeros without a branch.
-    // Every wave thus issues the same 2 KS vector loads per step, which keeps
-    // the compiler's wait counts exact: a stage is waited for only when it is
-    // deposited, SHD - 1 steps after its loads went out.
-    constexpr int PER = 2 * KS;                      // chunks per thread per step
+    u32x4* vst = kst + NSL * KS * TCH;
+    // Loads: wave w takes block w / 4 of each tile of a step, rows
+    // 4 (w % 4) .. 4 (w % 4) + 3 of it, from K and from V. Its block is one
+    // block-table entry, read by a scalar load one step ahead; the buffer
+    // resources are zero bytes long for blocks past the end and V rows at
+    // or past kmax read past the block, so those arrive as zeros. Every wave
+    // issues the same 2 KS loads per step; a step's loads are waited for
+    // (vmcnt, counted by hand: the compiler does not track writes to LDS
+    // that come from loads) at the end of the iteration before its math.
     constexpr uint32_t kBlockBytes = (uint32_t)(kBS * D * sizeof(T));
     const int tid = (int)threadIdx.x;
     const int bw = w / (NW / TB);                     // this wave's block within a tile
-    const int lrow = (tid >> 4) & 15, lc = tid & 15;
-    const int loff = (lrow * D + lc * 8) * (int)sizeof(T);
-    u32x4* kdst = kst + (bw * 16 + lrow) * KCH + (lc ^ lrow);
-    u32x4* vdst = vst + (bw * 16 + lrow) * RSV + lc;
+    const int lrow = (tid >> 4) & 15, lp = tid & 15;  // row in the block, LDS position in the row
+    const int koff = (lrow * D + (lp ^ lrow) * 8) * (int)sizeof(T);
+    const int voff = (lrow * D + (lp ^ (2 * (lrow & 7))) * 8) * (int)sizeof(T);
+    const int wrow0 = bw * 16 + (lrow & ~3);          // first LDS row this wave writes
     // The block table through the constant address space: a uniform load
     // from there is a scalar load, waited for by the barrier's counter
     // rather than behind the vector loads in flight.
@@ -450,7 +479,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     int id_next[KS];
 #pragma unroll
     for (int j = 0; j < KS; ++j) id_next[j] = block_id(j);
-    auto fetch = [&](u32x4 (&st)[PER], int step) {
+    auto fetch = [&](int step, u32x4* k_next, u32x4* v_next) {  // the step's tiles into an LDS slot
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
         const int u = step * KS + j;
@@ -462,86 +491,109 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
         const uint32_t n = ok ? kBlockBytes : 0u;
         const __amdgpu_buffer_rsrc_t kr = block_rsrc(kbase + off, n);
         const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + off, n);
-        st[2 * j] = __builtin_amdgcn_raw_buffer_load_b128(kr, loff, 0, 0);
-        st[2 * j + 1] =
-            __builtin_amdgcn_raw_buffer_load_b128(vr, blk * kBS + lrow < kmax ? loff : (int)kBlockBytes, 0, 0);
+        const int rows = j * TCH + wrow0 * KCH;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(k_next + rows), 16,
+                                                 koff, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(v_next + rows), 16,
+                                                 blk * kBS + lrow < kmax ? voff : (int)kBlockBytes, 0, 0, 0);
       }
     };
-    auto deposit = [&](const u32x4 (&st)[PER], int step) {
+    int klo[KK];                                      // lane offsets (chunks) of the K operand reads
 #pragma unroll
-      for (int j = 0; j < KS; ++j) {
-        kdst[((step & 1) * KS + j) * STGK] = st[2 * j];
-        vdst[((step & 1) * KS + j) * STGV] = st[2 * j + 1];
-      }
-    };
-    const u32x4* klane[KK];                                                // + tile slot*STGK + b*16*KCH
+    for (int kk = 0; kk < KK; ++kk) klo[kk] = g * KCH + ((4 * kk + grp) ^ g);
+    int vlo[NACC];                                    // lane offsets (bytes) of the V transpose reads
 #pragma unroll
-    for (int kk = 0; kk < KK; ++kk) klane[kk] = kst + g * KCH + ((4 * kk + grp) ^ g);
-    const char* vlane = reinterpret_cast<const char*>(vst) +
-                        ((4 * grp + (g >> 2)) * RSV + ((g >> 1) & 1)) * 16 + (g & 1) * 8;  // + 32 mt
-    auto qk_tile = [&](int slot, f32x4 (&sc)[NTW][TB]) {  // QK scores of the tile in LDS tile slot `slot`
+    for (int mt = 0; mt < NACC; ++mt) {
+      const int R = 4 * grp + (g >> 2);
+      vlo[mt] = (R * KCH + 2 * (mt ^ (R & 7)) + ((g >> 1) & 1)) * 16 + (g & 1) * 8;
+    }
+    auto qk_tile = [&](const u32x4* kt, f32x4 (&sc)[NTW][TB]) {  // QK scores of the K tile at kt
       tx8 ka[TB][KK];
 #pragma unroll
       for (int b = 0; b < TB; ++b)
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) ka[b][kk] = __builtin_bit_cast(tx8, klane[kk][slot * STGK + b * 16 * KCH]);
+        for (int kk = 0; kk < KK; ++kk) ka[b][kk] = __builtin_bit_cast(tx8, kt[klo[kk] + b * 16 * KCH]);
 #pragma unroll
       for (int jj = 0; jj < NTW; ++jj) qk_scores(ka, jj, sc[jj]);
     };
-    // Softmax and P.V of key tile u from its scores and LDS tile slot
-    // `slot`. V^T operand of M-tile mt (head dims 16mt .. 16mt+15): keys
-    // 4grp .. 4grp+3 of block 0 and the same of block 1, in the order the QK
-    // accumulator hands P over.
-    auto pv_tile = [&](int slot, int u, const f32x4 (&sc)[NTW][TB]) {
-      const char* vs = vlane + (size_t)slot * STGV * 16;
-      tx8 vo[NACC];
-#pragma unroll
-      for (int mt = 0; mt < NACC; ++mt) {
-        const i16x4 lo = lds_read_tr16(vs + 32 * mt);
-        const i16x4 hi = lds_read_tr16(vs + 16 * RSV * 16 + 32 * mt);
-        vo[mt] = __builtin_bit_cast(tx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-      }
+    // Softmax of key tile u from its scores: P of each N-tile as the B
+    // operand of the P.V products (the accumulators are rescaled here).
+    auto softmax_pack = [&](int u, const f32x4 (&sc)[NTW][TB], tx8 (&pv)[NTW]) {
 #pragma unroll
       for (int jj = 0; jj < NTW; ++jj) {
         T pb[TB][4];
         softmax_step(sc[jj], jj, u, pb);
-        const tx8 pv = pack_p2(pb);
-#pragma unroll
-        for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma32(vo[mt], pv, acc[jj][mt]);
-        accl[jj] = H16<T>::mma32(ones8, pv, accl[jj]);
+        pv[jj] = pack_p2(pb);
       }
     };
-    // Step σ arrives in register stage σ % SHD. Iteration σ refills stage
-    // σ % SHD (step σ went to LDS in the previous iteration) with step
-    // σ + SHD, runs the QK products, softmax and P.V products of this wave's
-    // tile σ KS + kg from LDS slot σ & 1, moves step σ + 1 from its stage into
-    // the other slot, and ends with one barrier. The loop runs in whole
-    // groups of SHD (stage indices are compile-time); iterations past the
-    // last step only load nothing and deposit zeros. (Running the next
-    // tile's QK products ahead of this tile's softmax measured no faster.)
-    static_assert(SHD >= 2, "one step in LDS, at least one more in flight");
-    const int nsteps = (ntiles + KS - 1) / KS;
-    u32x4 stage[SHD][PER];
+    // P.V products (and row sums) from V tile slot tslot. V^T operand of
+    // M-tile mt (head dims 16mt .. 16mt+15): keys 4grp .. 4grp+3 of block 0
+    // and the same of block 1, in the order the QK accumulator hands P over.
+    auto pv_apply = [&](const u32x4* vt, const tx8 (&pv)[NTW]) {
+      const char* vb = reinterpret_cast<const char*>(vt);
+      tx8 vo[NACC];
 #pragma unroll
-    for (int d = 0; d < SHD; ++d) fetch(stage[d], d);
-    deposit(stage[0], 0);
-    __syncthreads();
-    for (int s0 = 0; s0 < nsteps; s0 += SHD) {
-      auto iteration = [&](auto d_const) {
-        constexpr int d = decltype(d_const)::value;
-        const int step = s0 + d;
-        fetch(stage[d], step + SHD);
-        const int t = step * KS + kg;
-        if (t < ntiles) {
-          f32x4 sc[NTW][TB];
-          qk_tile((step & 1) * KS + kg, sc);
-          pv_tile((step & 1) * KS + kg, t, sc);
-        }
-        deposit(stage[(d + 1) % SHD], step + 1);
-        __syncthreads();
-      };
-      unrolled<SHD>(iteration);
+      for (int mt = 0; mt < NACC; ++mt) {
+        const i16x4 lo = lds_read_tr16(vb + vlo[mt]);
+        const i16x4 hi = lds_read_tr16(vb + vlo[mt] + 16 * KCH * 16);
+        vo[mt] = __builtin_bit_cast(tx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+      }
+#pragma unroll
+      for (int jj = 0; jj < NTW; ++jj) {
+#pragma unroll
+        for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma32(vo[mt], pv[jj], acc[jj][mt]);
+        accl[jj] = H16<T>::mma32(ones8, pv[jj], accl[jj]);
+      }
+    };
+    // Iteration σ (slot σ % NSL) starts the loads of step σ + 2, runs this
+    // wave's share of the math, waits for the loads of step σ + 1 and ends
+    // with one barrier. A wave of key group 0 runs its tile σ KS in order:
+    // QK products, softmax, P.V products. With a key split, the two waves
+    // that share a SIMD (w and w + NW/2) are in different key groups, and
+    // key group 1 runs the P.V products of its previous tile first, then the
+    // QK products and softmax of this one: while one wave of a SIMD has the
+    // matrix unit, the other mostly has the vector unit, where the same
+    // order in both would queue them on one unit at a time. The loop runs in
+    // whole groups of NSL; iterations past the last step load nothing, and
+    // one extra iteration lets key group 1 finish.
+    const int nsteps = (ntiles + KS - 1) / KS;
+    const int niter = nsteps + (KS > 1 ? 1 : 0);
+    {
+      auto f0 = [&](u32x4* kn, u32x4* vn) { fetch(0, kn, vn); };
+      auto f1 = [&](u32x4* kn, u32x4* vn) { fetch(1, kn, vn); };
+      auto none = [](const u32x4*, const u32x4*, const u32x4*) {};
+      with_slots(kst, vst, kst + 2 * KS * TCH, vst + 2 * KS * TCH, vst + 3 * KS * TCH, f0, none);
+      with_slots(kst + KS * TCH, vst + KS * TCH, kst + 2 * KS * TCH, vst + 2 * KS * TCH, vst + 3 * KS * TCH, f1, none);
     }
+    lds_barrier<2 * KS>();  // step 0 is in LDS
+    tx8 pv[NTW];  // P of this wave's tile (key group 1: applied one step late)
+    for (int s0 = 0; s0 < niter; s0 += NSL) {
+      auto iteration = [&](auto d_const) {
+        constexpr int d = decltype(d_const)::value;  // == step % NSL
+        const int step = s0 + d;
+        const int t = step * KS + kg;
+        const bool late = KS > 1 && kg > 0;
+        auto load = [&](u32x4* kn, u32x4* vn) { fetch(step + 2, kn, vn); };
+        auto math = [&](const u32x4* kc, const u32x4* vc, const u32x4* vp) {
+          if (late && step > 0 && t - KS < ntiles) pv_apply(vp, pv);
+          if (t < ntiles) {
+            f32x4 sc[NTW][TB];
+            qk_tile(kc, sc);
+            softmax_pack(t, sc, pv);
+            if (!late) pv_apply(vc, pv);
+          }
+        };
+        constexpr int nx = (d + 2) % NSL, pr = (d + NSL - 1) % NSL;
+        with_slots(kst + nx * KS * TCH, vst + nx * KS * TCH, kst + (d * KS + kg) * TCH, vst + (d * KS + kg) * TCH,
+                   vst + (pr * KS + kg) * TCH, load, math);
+        lds_barrier<2 * KS>();  // step σ + 1 is in LDS
+      };
+      unrolled<NSL>(iteration);
+    }
+    // Nothing may still land in LDS once it is reused: each wave drains its
+    // loads (those past the last step write zeros), then a barrier.
+    __builtin_amdgcn_s_waitcnt(0x7 << 4);  // vmcnt(0) lgkmcnt(0)
+    if constexpr (KS > 1) __syncthreads();
     if constexpr (KS > 1) {
       // Key groups 1 .. KS-1 hand (max, P.V accumulators, row sums) to key
       // group 0 through LDS (free again after the loop's last barrier), which
@@ -634,20 +686,20 @@ template <typename T>
 hipError_t launch_prefill_t(PrefillParams P, int D, int maxq, const Launch& L) {
   const int64_t pairs = (int64_t)P.S * P.Hkv;
   auto tiles = [&](int rows) { const int qt = rows / P.G; return pairs * ((maxq + qt - 1) / qt); };
-  constexpr size_t kSlots = (size_t)2 * 2 * 16 * (2 * (128 / 8) + 2) * 16;  // two slots of a K and (padded) V tile
+  constexpr size_t kTile = (size_t)2 * 16 * (128 / 8) * 16;  // one K or V tile: two blocks of 16 rows
   if (D == 128) {
     if (tiles(128) <= kPrefillSmallGrid) {
       constexpr int NW = 8, NTW = 2, TB = 2, KS = 2;
       P.QT = 128 / P.G;
       const size_t merge = (size_t)(KS - 1) * (NW / KS) * (NTW * (8 + 1) + 1) * 64 * 16;
-      const size_t smem = std::max((size_t)KS * kSlots, merge);
+      const size_t smem = std::max((size_t)4 * KS * 2 * kTile, merge);  // four slots of K and V
       return launch_lds<pa_prefill_h16<T, 128, NW, NTW, TB, true, 2, KS>>(smem, dim3((unsigned)tiles(128)),
                                                                            dim3(NW * 64), smem, L, P);
     }
     constexpr int NW = 8, NTW = 2, TB = 2;
     P.QT = 256 / P.G;
-    return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true, 2, 1>, dim3((unsigned)tiles(256)), dim3(NW * 64), kSlots,
-                  L, P);
+    return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true, 2, 1>, dim3((unsigned)tiles(256)), dim3(NW * 64),
+                  4 * 2 * kTile, L, P);
   }
   constexpr int NW = 8, NTW = 1, TB = 1;
   P.QT = 128 / P.G;
