@@ -442,9 +442,9 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     constexpr int TCH = TB * 16 * KCH;               // chunks per K (or V) tile
     // LDS: NSL slots (step % NSL) of KS tiles each, K [NSL][KS][TB*16][16]
     // then V [NSL][KS][TB*16][16]. A step is KS consecutive key tiles, one
-    // per key group. Step σ + 2 loads while step σ is computed; with a key
-    // split, key group 1 reads V of step σ - 1 during step σ (below): four
-    // slots cover both, and make every slot index a compile-time constant.
+    // per key group. Step σ + 2 loads while step σ is computed, and half the
+    // waves read V of step σ - 1 during step σ (below): four slots cover
+    // both, and make every slot index a compile-time constant.
     constexpr int NSL = 4;
     constexpr int SHD_ = 2;
     static_assert(SHD == SHD_, "the shared form prefetches two steps");
@@ -547,17 +547,16 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     };
     // Iteration σ (slot σ % NSL) starts the loads of step σ + 2, runs this
     // wave's share of the math, waits for the loads of step σ + 1 and ends
-    // with one barrier. A wave of key group 0 runs its tile σ KS in order:
-    // QK products, softmax, P.V products. With a key split, the two waves
-    // that share a SIMD (w and w + NW/2) are in different key groups, and
-    // key group 1 runs the P.V products of its previous tile first, then the
-    // QK products and softmax of this one: while one wave of a SIMD has the
+    // with one barrier. Waves w < NW/2 run their tile of the step in order:
+    // QK products, softmax, P.V products. Their SIMD partners (w + NW/2)
+    // run the P.V products of their previous tile first, then the QK
+    // products and softmax of this one: while one wave of a SIMD has the
     // matrix unit, the other mostly has the vector unit, where the same
     // order in both would queue them on one unit at a time. The loop runs in
     // whole groups of NSL; iterations past the last step load nothing, and
-    // one extra iteration lets key group 1 finish.
+    // one extra iteration lets the late waves finish.
     const int nsteps = (ntiles + KS - 1) / KS;
-    const int niter = nsteps + (KS > 1 ? 1 : 0);
+    const int niter = nsteps + 1;
     {
       auto f0 = [&](u32x4* kn, u32x4* vn) { fetch(0, kn, vn); };
       auto f1 = [&](u32x4* kn, u32x4* vn) { fetch(1, kn, vn); };
@@ -566,13 +565,13 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
       with_slots(kst + KS * TCH, vst + KS * TCH, kst + 2 * KS * TCH, vst + 2 * KS * TCH, vst + 3 * KS * TCH, f1, none);
     }
     lds_barrier<2 * KS>();  // step 0 is in LDS
-    tx8 pv[NTW];  // P of this wave's tile (key group 1: applied one step late)
+    tx8 pv[NTW];  // P of this wave's tile (late waves: applied one step later)
     for (int s0 = 0; s0 < niter; s0 += NSL) {
       auto iteration = [&](auto d_const) {
         constexpr int d = decltype(d_const)::value;  // == step % NSL
         const int step = s0 + d;
         const int t = step * KS + kg;
-        const bool late = KS > 1 && kg > 0;
+        const bool late = w >= NW / 2;
         auto load = [&](u32x4* kn, u32x4* vn) { fetch(step + 2, kn, vn); };
         auto math = [&](const u32x4* kc, const u32x4* vc, const u32x4* vp) {
           if (late && step > 0 && t - KS < ntiles) pv_apply(vp, pv);
