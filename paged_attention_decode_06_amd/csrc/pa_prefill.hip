@@ -21,17 +21,16 @@ namespace {
 // The decode tile layout carries over with query rows on the MFMA N axis: a
 // row is one (chunk token, query head of the GQA group), row = token * G +
 // head, so one K/V tile serves every head of the group and QT tokens. One
-// workgroup takes (sequence, KV head, QT-token query tile); each of its NW
-// waves owns NTW N-tiles of 16 rows and walks every key tile itself (no merge
-// across waves). In the shared form (head_dim 128) the workgroup stages each
-// K/V tile once into one of two LDS buffers (K XOR-swizzled by row so the
-// token-wise operand reads hit distinct banks, V read back transposed), with
-// the loads of the next SHD tiles already in flight in registers; every wave
-// reads its operands there. In the per-wave form (head_dim 256) each wave
-// loads its own tile, passes K through a wave-private swizzled LDS tile and
-// transposes V in registers. P is the QK accumulator rounded to the 16-bit
-// type; its row sums come from one more MFMA against a ones operand. Outputs
-// are stored straight from the accumulators.
+// workgroup takes (sequence, KV head, QT-token query tile). Its NW waves
+// form KS key groups of NW / KS row groups; each wave owns NTW N-tiles of
+// 16 rows and, of every KS consecutive key tiles, the one of its key group
+// (with KS = 2 the two key groups merge their partial results at the end).
+// The workgroup loads each K/V tile once, straight from memory into LDS,
+// and every wave reads its MFMA operands there (K row-permuted so the
+// token-wise operand reads hit distinct banks, V read back transposed). P is
+// the QK accumulator rounded to the 16-bit type; its row sums come from one
+// more MFMA against a ones operand. Outputs are stored straight from the
+// accumulators.
 // Max over the four lane groups (lanes l, l^16, l^32, l^48: the same row)
 // with the gfx950 lane-swap moves instead of LDS-routed shuffles.
 // v_permlane16_swap a, b exchanges rows 1/3 of a with rows 0/2 of b; with b a
@@ -111,22 +110,20 @@ struct PrefillParams {
   float scale2;
 };
 
-template <typename T, int D, int NW, int NTW, int TB, bool SH, int SHD, int KS>
+template <typename T, int D, int NW, int NTW, int TB, int SHD, int KS>
 __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   typedef typename H16<T>::x8 tx8;
   typedef typename H16<T>::x4 tx4;
   extern __shared__ float smem[];
   constexpr int KK = D / 32;    // QK MFMAs per block and N-tile
-  constexpr int NH = D / 128;
-  constexpr int NACC = NH * 8;  // output tiles per N-tile
-  constexpr int CH = 64 / TB;   // tiles per block-id refill
-  constexpr int KCH = D / 8;
+  constexpr int NACC = D / 16;  // output tiles (16 head dims each) per N-tile
+  constexpr int KCH = D / 8;    // 16-byte chunks per head_dim row
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane & 15, grp = lane >> 4;
   // Key split: the waves form KS groups of NW / KS; wave w takes row group
   // w % (NW / KS) and, of every KS consecutive key tiles, tile w / (NW / KS).
-  static_assert(KS == 1 || (SH && NW % KS == 0), "key split: shared form only");
+  static_assert(NW % KS == 0, "key groups of equal size");
   constexpr int NWR = NW / KS;  // waves per key group (row groups)
   const int rg = w % NWR, kg = w / NWR;
 
@@ -208,7 +205,6 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     }
   }
 
-  u32x4* ktile = reinterpret_cast<u32x4*>(smem) + (size_t)w * TB * 16 * KCH;
   const int64_t head_elems = (int64_t)kBS * D;
   const int64_t block_elems = head_elems * P.Hkv;
   const T* kbase = reinterpret_cast<const T*>(P.k) + kvh * head_elems;
@@ -237,38 +233,10 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) ones4[i] = (T)1.0f;
 
-  // Physical ids of the next CH tiles: lane j holds block (k * CH * TB + j).
-  int ids = 0;
-  auto refill = [&](int k) {
-    const int blk = k * CH * TB + lane;
-    int id = -1;
-    if (lane < CH * TB && blk < nblk) {
-      id = bt_row[blk];
-      if ((uint64_t)(int64_t)id >= (uint64_t)P.NB) id = 0;  // out-of-range ids read block 0
-    }
-    ids = id;
-  };
-
-  // Issues tile t's loads (tiles are issued in order, so the id list is
-  // refilled exactly when a new CH-tile chunk starts).
-  auto issue = [&](BTile<D, TB>& tl, int t) {
-    if (t % CH == 0) refill(t / CH);
-    int64_t phys[TB];
-    bool vb[TB];
-#pragma unroll
-    for (int b = 0; b < TB; ++b) {
-      vb[b] = t * TB + b < nblk;
-      phys[b] = __builtin_amdgcn_readlane(ids, (t % CH) * TB + b);
-    }
-    issue_tile<T, D, TB, false>(tl, kbase, vbase, block_elems, phys, vb, g, grp);
-  };
-
   // The math of tile t in three steps: the QK scores of N-tile jj from K
   // operands ka; the online-softmax update of that N-tile (running max,
   // exp-sum, rescale of its accumulators), which hands back P rounded to the
-  // 16-bit type; and P.V. The shared form runs the steps of consecutive
-  // tiles interleaved; the per-wave form runs them in order (compute_ops).
-  static_assert(!SH || TB == 2, "the shared form takes two-block tiles");
+  // 16-bit type; and P.V (below, per tile shape).
   auto qk_scores = [&](const tx8 (&ka)[TB][KK], int jj, f32x4 (&sc)[TB]) {
 #pragma unroll
     for (int b = 0; b < TB; ++b) {
@@ -336,112 +304,28 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     return pv;
   };
 
-  // Per-wave form: P.V from the tile's raw V rows, transposed in registers.
-  // V rows at or past kmax (tail slots of the last block, blocks past the
-  // end) are zeroed first: a zero weight times NaN would poison the sum.
-  auto compute_ops = [&](tx8 (&ka)[TB][KK], BTile<D, TB>& tl, int t) {
-    const int tok0 = t * TB * kBS;
-    if (tok0 + TB * kBS > kmax) {
-#pragma unroll
-      for (int b = 0; b < TB; ++b)
-#pragma unroll
-        for (int rr = 0; rr < 4; ++rr)
-          if (tok0 + b * kBS + 4 * grp + rr >= kmax)
-#pragma unroll
-            for (int h = 0; h < NH; ++h) tl.v[b][rr][h] = (u32x4){0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int jj = 0; jj < NTW; ++jj) {
-      f32x4 sc[TB];
-      T pb[TB][4];
-      qk_scores(ka, jj, sc);
-      softmax_step(sc, jj, t, pb);
-      if constexpr (TB == 2) {
-        const tx8 pv = pack_p2(pb);
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int c = j >> 1;
-            u32x4 a;
-            if (j & 1) {
-              a[0] = pack_hi(tl.v[0][0][h][c], tl.v[0][1][h][c]);
-              a[1] = pack_hi(tl.v[0][2][h][c], tl.v[0][3][h][c]);
-              a[2] = pack_hi(tl.v[1][0][h][c], tl.v[1][1][h][c]);
-              a[3] = pack_hi(tl.v[1][2][h][c], tl.v[1][3][h][c]);
-            } else {
-              a[0] = pack_lo(tl.v[0][0][h][c], tl.v[0][1][h][c]);
-              a[1] = pack_lo(tl.v[0][2][h][c], tl.v[0][3][h][c]);
-              a[2] = pack_lo(tl.v[1][0][h][c], tl.v[1][1][h][c]);
-              a[3] = pack_lo(tl.v[1][2][h][c], tl.v[1][3][h][c]);
-            }
-            acc[jj][h * 8 + j] = H16<T>::mma32(__builtin_bit_cast(tx8, a), pv, acc[jj][h * 8 + j]);
-          }
-        accl[jj] = H16<T>::mma32(ones8, pv, accl[jj]);
-      } else {
-        tx4 pv4;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pv4[i] = pb[0][i];
-#pragma unroll
-        for (int h = 0; h < NH; ++h)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const int c = j >> 1;
-            u32x2 a;
-            if (j & 1) {
-              a[0] = pack_hi(tl.v[0][0][h][c], tl.v[0][1][h][c]);
-              a[1] = pack_hi(tl.v[0][2][h][c], tl.v[0][3][h][c]);
-            } else {
-              a[0] = pack_lo(tl.v[0][0][h][c], tl.v[0][1][h][c]);
-              a[1] = pack_lo(tl.v[0][2][h][c], tl.v[0][3][h][c]);
-            }
-            acc[jj][h * 8 + j] = H16<T>::mma16(__builtin_bit_cast(tx4, a), pv4, acc[jj][h * 8 + j]);
-          }
-        accl[jj] = H16<T>::mma16(ones4, pv4, accl[jj]);
-      }
-    }
-  };
-
-  // Per-wave path: the wave's own K tile goes registers -> its LDS tile ->
-  // MFMA A operands.
-  auto compute = [&](BTile<D, TB>& tl, int t) {
-#pragma unroll
-    for (int b = 0; b < TB; ++b)
-#pragma unroll
-      for (int rr = 0; rr < 4; ++rr)
-#pragma unroll
-        for (int h = 0; h < NH; ++h) {
-          const int row = 4 * grp + rr, c16 = 16 * h + g;
-          ktile[(b * 16 + row) * KCH + (c16 ^ row)] = tl.k[b][rr][h];
-        }
-    tx8 ka[TB][KK];
-#pragma unroll
-    for (int b = 0; b < TB; ++b)
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) {
-        const int c16 = 4 * kk + grp;
-        ka[b][kk] = __builtin_bit_cast(tx8, ktile[(b * 16 + g) * KCH + (c16 ^ g)]);
-      }
-    compute_ops(ka, tl, t);
-  };
-
-  if constexpr (SH) {
-    // Shared path: the workgroup loads each K/V tile once into LDS and every
+  {
+    // The workgroup loads each K/V tile once into LDS and every
     // wave reads its MFMA operands there. The loads go straight from memory
     // into LDS (buffer loads with the LDS flag: a wave's 64 lanes write 1 KB
     // at the wave's LDS address, lane L at +16 L), so no registers stage the
-    // tiles and no stores move them. LDS rows are 16 chunks of 16 bytes,
-    // permuted by row so that both operand reads are free of bank conflicts:
-    // K row r keeps chunk c at position c ^ r (the 16 rows a K read takes
-    // hit 16 distinct positions); V row r keeps chunk c at c ^ 2 (r % 8) (the
-    // transpose read takes chunk pairs 2mt, 2mt+1 from rows 4grp .. 4grp+3,
-    // and eight consecutive rows then hit eight distinct 32-byte bank
-    // groups). Each lane loads the global chunk that its LDS position holds.
-    static_assert(KCH == 16, "the permutations span the 16 chunks of a 128-dim row");
-    static_assert(TB == 2 && NW * 64 == TB * 16 * KCH, "per tile, one K and one V chunk per lane");
+    // tiles and no stores move them. LDS rows are the KCH 16-byte chunks of
+    // a head_dim row, permuted by row so that both operand reads are free of
+    // bank conflicts: K row r keeps chunk c at position c ^ (r % 16) (the 16
+    // rows a K read takes hit 16 distinct positions mod 16); V row r keeps
+    // chunk c at c ^ 2 (r % 8) (the transpose read takes chunk pairs 2mt,
+    // 2mt+1 from rows 4grp .. 4grp+3, and eight consecutive rows then hit
+    // eight distinct 32-byte bank groups). Each lane loads the global chunk
+    // that its LDS position holds. A tile is two blocks at head_dim 128 (32
+    // keys, 16x16x32 P.V products) and one block at head_dim 256 (16 keys,
+    // 16x16x16 P.V products): 8 KB of K and 8 KB of V either way.
+    static_assert(KCH == 16 || KCH == 32, "head_dim 128 or 256");
+    static_assert(NW * 64 == TB * 16 * KCH, "per tile, one K and one V chunk per lane");
     constexpr int TCH = TB * 16 * KCH;               // chunks per K (or V) tile
-    // LDS: NSL slots (step % NSL) of KS tiles each, K [NSL][KS][TB*16][16]
-    // then V [NSL][KS][TB*16][16]. A step is KS consecutive key tiles, one
+    constexpr int RPW = 64 / KCH;                    // tile rows one wave loads
+    using PV = std::conditional_t<TB == 2, tx8, tx4>;  // P as the B operand of a P.V product
+    // LDS: NSL slots (step % NSL) of KS tiles each, K [NSL][KS][TB*16][KCH]
+    // then V [NSL][KS][TB*16][KCH]. A step is KS consecutive key tiles, one
     // per key group. Step σ + 2 loads while step σ is computed, and half the
     // waves read V of step σ - 1 during step σ (below): four slots cover
     // both, and make every slot index a compile-time constant.
@@ -450,8 +334,8 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     static_assert(SHD == SHD_, "the shared form prefetches two steps");
     u32x4* kst = reinterpret_cast<u32x4*>(smem);
     u32x4* vst = kst + NSL * KS * TCH;
-    // Loads: wave w takes block w / 4 of each tile of a step, rows
-    // 4 (w % 4) .. 4 (w % 4) + 3 of it, from K and from V. Its block is one
+    // Loads: wave w takes tile rows w RPW .. w RPW + RPW - 1 of each tile of
+    // a step (all in one block), from K and from V. Its block is one
     // block-table entry, read by a scalar load one step ahead; the buffer
     // resources are zero bytes long for blocks past the end and V rows at
     // or past kmax read past the block, so those arrive as zeros. Every wave
@@ -459,12 +343,11 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     // (vmcnt, counted by hand: the compiler does not track writes to LDS
     // that come from loads) at the end of the iteration before its math.
     constexpr uint32_t kBlockBytes = (uint32_t)(kBS * D * sizeof(T));
-    const int tid = (int)threadIdx.x;
-    const int bw = w / (NW / TB);                     // this wave's block within a tile
-    const int lrow = (tid >> 4) & 15, lp = tid & 15;  // row in the block, LDS position in the row
+    const int wrow0 = w * RPW;                        // first tile row this wave writes
+    const int bw = wrow0 / 16;                        // this wave's block within a tile
+    const int lrow = (wrow0 + lane / KCH) % 16, lp = lane % KCH;  // row in the block, LDS position in the row
     const int koff = (lrow * D + (lp ^ lrow) * 8) * (int)sizeof(T);
     const int voff = (lrow * D + (lp ^ (2 * (lrow & 7))) * 8) * (int)sizeof(T);
-    const int wrow0 = bw * 16 + (lrow & ~3);          // first LDS row this wave writes
     // The block table through the constant address space: a uniform load
     // from there is a scalar load, waited for by the barrier's counter
     // rather than behind the vector loads in flight.
@@ -518,31 +401,47 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     };
     // Softmax of key tile u from its scores: P of each N-tile as the B
     // operand of the P.V products (the accumulators are rescaled here).
-    auto softmax_pack = [&](int u, const f32x4 (&sc)[NTW][TB], tx8 (&pv)[NTW]) {
+    auto softmax_pack = [&](int u, const f32x4 (&sc)[NTW][TB], PV (&pv)[NTW]) {
 #pragma unroll
       for (int jj = 0; jj < NTW; ++jj) {
         T pb[TB][4];
         softmax_step(sc[jj], jj, u, pb);
-        pv[jj] = pack_p2(pb);
+        if constexpr (TB == 2) {
+          pv[jj] = pack_p2(pb);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pv[jj][i] = pb[0][i];
+        }
       }
     };
-    // P.V products (and row sums) from V tile slot tslot. V^T operand of
+    // P.V products (and row sums) from the V tile at vt. V^T operand of
     // M-tile mt (head dims 16mt .. 16mt+15): keys 4grp .. 4grp+3 of block 0
-    // and the same of block 1, in the order the QK accumulator hands P over.
-    auto pv_apply = [&](const u32x4* vt, const tx8 (&pv)[NTW]) {
+    // (and the same of block 1 for two-block tiles), in the order the QK
+    // accumulator hands P over.
+    auto pv_apply = [&](const u32x4* vt, const PV (&pv)[NTW]) {
       const char* vb = reinterpret_cast<const char*>(vt);
-      tx8 vo[NACC];
+      PV vo[NACC];
 #pragma unroll
       for (int mt = 0; mt < NACC; ++mt) {
         const i16x4 lo = lds_read_tr16(vb + vlo[mt]);
-        const i16x4 hi = lds_read_tr16(vb + vlo[mt] + 16 * KCH * 16);
-        vo[mt] = __builtin_bit_cast(tx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        if constexpr (TB == 2) {
+          const i16x4 hi = lds_read_tr16(vb + vlo[mt] + 16 * KCH * 16);
+          vo[mt] = __builtin_bit_cast(tx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+        } else {
+          vo[mt] = __builtin_bit_cast(tx4, lo);
+        }
       }
 #pragma unroll
       for (int jj = 0; jj < NTW; ++jj) {
+        if constexpr (TB == 2) {
 #pragma unroll
-        for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma32(vo[mt], pv[jj], acc[jj][mt]);
-        accl[jj] = H16<T>::mma32(ones8, pv[jj], accl[jj]);
+          for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma32(vo[mt], pv[jj], acc[jj][mt]);
+          accl[jj] = H16<T>::mma32(ones8, pv[jj], accl[jj]);
+        } else {
+#pragma unroll
+          for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma16(vo[mt], pv[jj], acc[jj][mt]);
+          accl[jj] = H16<T>::mma16(ones4, pv[jj], accl[jj]);
+        }
       }
     };
     // Iteration σ (slot σ % NSL) starts the loads of step σ + 2, runs this
@@ -565,7 +464,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
       with_slots(kst + KS * TCH, vst + KS * TCH, kst + 2 * KS * TCH, vst + 2 * KS * TCH, vst + 3 * KS * TCH, f1, none);
     }
     lds_barrier<2 * KS>();  // step 0 is in LDS
-    tx8 pv[NTW];  // P of this wave's tile (late waves: applied one step later)
+    PV pv[NTW];  // P of this wave's tile (late waves: applied one step later)
     for (int s0 = 0; s0 < niter; s0 += NSL) {
       auto iteration = [&](auto d_const) {
         constexpr int d = decltype(d_const)::value;  // == step % NSL
@@ -631,53 +530,32 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
         }
       }
     }
-  } else {
-    BTile<D, TB> A;
-    issue(A, 0);
-    for (int t = 0;;) {
-      compute(A, t);
-      if (++t >= ntiles) break;
-      issue(A, t);
-    }
   }
 
-  // Per-wave form: acc[jj][h*8 + j][i] holds dim 128h + 32*grp + 8i + j of
-  // the lane's row (for fixed (h, i) the 8 values j = 0..7 are consecutive
-  // dims). Shared form: acc[jj][mt][i] holds dim 16mt + 4grp + i.
+  // acc[jj][mt][i] holds dim 16mt + 4grp + i of the lane's row; every lane
+  // of a row holds its sum.
 #pragma unroll
   for (int jj = 0; jj < NTW; ++jj) {
-    const float tot = accl[jj][0];
     if (!valid[jj]) continue;
-    const float inv = live[jj] ? 1.f / tot : 0.f;
+    const float inv = live[jj] ? 1.f / accl[jj][0] : 0.f;
     T* orow = out_row(jj);
-    if constexpr (SH) {  // acc[jj][mt][i] holds dim 16mt + 4grp + i
 #pragma unroll
-      for (int mt = 0; mt < NACC; ++mt) store4<T>(orow, 16 * mt + 4 * grp, acc[jj][mt] * inv);
-      continue;
-    }
-#pragma unroll
-    for (int h = 0; h < NH; ++h)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        typename H16<T>::x8 o;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) o[j] = (T)(acc[jj][h * 8 + j][i] * inv);
-        *reinterpret_cast<typename H16<T>::x8*>(orow + 128 * h + 32 * grp + 8 * i) = o;
-      }
+    for (int mt = 0; mt < NACC; ++mt) store4<T>(orow, 16 * mt + 4 * grp, acc[jj][mt] * inv);
   }
 }
 
-// Prefill launch shapes (measured on the four prefill workloads against the
-// other combinations of waves, N-tiles per wave, tile blocks, prefetch depth
-// and shared/per-wave tiles):
+// Prefill launch shapes (8 waves, two steps of K/V tiles in flight, measured
+// on the four prefill workloads against other wave, N-tile, tile, key-split
+// and prefetch choices):
 //   D = 128, at most kPrefillSmallGrid workgroups of 128 rows (long contexts,
-//     few query tiles): 8 waves x 1 N-tile, two-block tiles shared through
-//     LDS, 4 register stages of prefetch;
-//   D = 128, larger grids: 256 rows per workgroup, 8 waves x 2 N-tiles (half
-//     the LDS operand traffic per row), 2 register stages;
-//   D = 256: 128 rows, 8 waves x 1 N-tile, per-wave one-block tiles (the
-//     register budget of the wider rows).
-constexpr int kPrefillRows = 128;      // rows per workgroup of the smallest shape
+//     few query tiles): 4 row groups x 2 N-tiles x 2 key groups of two-block
+//     tiles, so that 256 workgroups still fill the chip with 32-row waves;
+//   D = 128, larger grids: 256 rows per workgroup, 8 waves x 2 N-tiles, no
+//     key split;
+//   D = 256: 64 rows per workgroup, 4 row groups x 1 N-tile x 2 key groups
+//     of one-block tiles (the register budget of the wider rows, and twice
+//     the workgroups to even out sequences of different lengths).
+constexpr int kPrefillRows = 64;       // rows per workgroup of the smallest shape
 constexpr int kPrefillMaxNW = 8;       // waves per workgroup, largest launch shape
 constexpr int64_t kPrefillSmallGrid = 512;
 
@@ -692,19 +570,20 @@ hipError_t launch_prefill_t(PrefillParams P, int D, int maxq, const Launch& L) {
       P.QT = 128 / P.G;
       const size_t merge = (size_t)(KS - 1) * (NW / KS) * (NTW * (8 + 1) + 1) * 64 * 16;
       const size_t smem = std::max((size_t)4 * KS * 2 * kTile, merge);  // four slots of K and V
-      return launch_lds<pa_prefill_h16<T, 128, NW, NTW, TB, true, 2, KS>>(smem, dim3((unsigned)tiles(128)),
+      return launch_lds<pa_prefill_h16<T, 128, NW, NTW, TB, 2, KS>>(smem, dim3((unsigned)tiles(128)),
                                                                            dim3(NW * 64), smem, L, P);
     }
     constexpr int NW = 8, NTW = 2, TB = 2;
     P.QT = 256 / P.G;
-    return launch(pa_prefill_h16<T, 128, NW, NTW, TB, true, 2, 1>, dim3((unsigned)tiles(256)), dim3(NW * 64),
+    return launch(pa_prefill_h16<T, 128, NW, NTW, TB, 2, 1>, dim3((unsigned)tiles(256)), dim3(NW * 64),
                   4 * 2 * kTile, L, P);
   }
-  constexpr int NW = 8, NTW = 1, TB = 1;
-  P.QT = 128 / P.G;
-  const size_t smem = (size_t)NW * TB * 16 * 256 * sizeof(T);
-  return launch(pa_prefill_h16<T, 256, NW, NTW, TB, false, 1, 1>, dim3((unsigned)tiles(128)), dim3(NW * 64), smem, L,
-                P);
+  constexpr int NW = 8, NTW = 1, TB = 1, KS = 2;
+  P.QT = 64 / P.G;
+  const size_t merge = (size_t)(KS - 1) * (NW / KS) * (NTW * (16 + 1) + 1) * 64 * 16;
+  const size_t smem = std::max((size_t)4 * KS * 2 * kTile, merge);  // four slots of K and V
+  return launch_lds<pa_prefill_h16<T, 256, NW, NTW, TB, 2, KS>>(smem, dim3((unsigned)tiles(64)), dim3(NW * 64),
+                                                                       smem, L, P);
 }
 
 int check_prefill(const void* out, const void* q, const void* k, const void* v, const int32_t* bt,
