@@ -326,12 +326,12 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     using PV = std::conditional_t<TB == 2, tx8, tx4>;  // P as the B operand of a P.V product
     // LDS: NSL slots (step % NSL) of KS tiles each, K [NSL][KS][TB*16][KCH]
     // then V [NSL][KS][TB*16][KCH]. A step is KS consecutive key tiles, one
-    // per key group. Step σ + 2 loads while step σ is computed, and half the
-    // waves read V of step σ - 1 during step σ (below): four slots cover
-    // both, and make every slot index a compile-time constant.
-    constexpr int NSL = 4;
-    constexpr int SHD_ = 2;
-    static_assert(SHD == SHD_, "the shared form prefetches two steps");
+    // per key group. Steps σ + 1 .. σ + SHD load while step σ is computed,
+    // and half the waves read V of step σ - 1 during step σ (below): SHD + 2
+    // slots cover both, and the loop runs in groups of NSL so that every slot
+    // index is a compile-time constant.
+    static_assert(SHD >= 2, "at least two steps in flight");
+    constexpr int NSL = SHD + 2;
     u32x4* kst = reinterpret_cast<u32x4*>(smem);
     u32x4* vst = kst + NSL * KS * TCH;
     // Loads: wave w takes tile rows w RPW .. w RPW + RPW - 1 of each tile of
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
         }
       }
     };
-    // Iteration σ (slot σ % NSL) starts the loads of step σ + 2, runs this
+    // Iteration σ (slot σ % NSL) starts the loads of step σ + SHD, runs this
     // wave's share of the math, waits for the loads of step σ + 1 and ends
     // with one barrier. Waves w < NW/2 run their tile of the step in order:
     // QK products, softmax, P.V products. Their SIMD partners (w + NW/2)
@@ -457,13 +457,16 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     const int nsteps = (ntiles + KS - 1) / KS;
     const int niter = nsteps + 1;
     {
-      auto f0 = [&](u32x4* kn, u32x4* vn) { fetch(0, kn, vn); };
-      auto f1 = [&](u32x4* kn, u32x4* vn) { fetch(1, kn, vn); };
       auto none = [](const u32x4*, const u32x4*, const u32x4*) {};
-      with_slots(kst, vst, kst + 2 * KS * TCH, vst + 2 * KS * TCH, vst + 3 * KS * TCH, f0, none);
-      with_slots(kst + KS * TCH, vst + KS * TCH, kst + 2 * KS * TCH, vst + 2 * KS * TCH, vst + 3 * KS * TCH, f1, none);
+      auto prologue = [&](auto d_const) {
+        constexpr int d = decltype(d_const)::value;
+        auto f = [&](u32x4* kn, u32x4* vn) { fetch(d, kn, vn); };
+        with_slots(kst + d * KS * TCH, vst + d * KS * TCH, kst + SHD * KS * TCH, vst + SHD * KS * TCH,
+                   vst + (SHD + 1) * KS * TCH, f, none);
+      };
+      unrolled<SHD>(prologue);
     }
-    lds_barrier<2 * KS>();  // step 0 is in LDS
+    lds_barrier<2 * KS * (SHD - 1)>();  // step 0 is in LDS
     PV pv[NTW];  // P of this wave's tile (late waves: applied one step later)
     for (int s0 = 0; s0 < niter; s0 += NSL) {
       auto iteration = [&](auto d_const) {
@@ -471,7 +474,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
         const int step = s0 + d;
         const int t = step * KS + kg;
         const bool late = w >= NW / 2;
-        auto load = [&](u32x4* kn, u32x4* vn) { fetch(step + 2, kn, vn); };
+        auto load = [&](u32x4* kn, u32x4* vn) { fetch(step + SHD, kn, vn); };
         auto math = [&](const u32x4* kc, const u32x4* vc, const u32x4* vp) {
           if (late && step > 0 && t - KS < ntiles) pv_apply(vp, pv);
           if (t < ntiles) {
@@ -481,10 +484,10 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
             if (!late) pv_apply(vc, pv);
           }
         };
-        constexpr int nx = (d + 2) % NSL, pr = (d + NSL - 1) % NSL;
+        constexpr int nx = (d + SHD) % NSL, pr = (d + NSL - 1) % NSL;
         with_slots(kst + nx * KS * TCH, vst + nx * KS * TCH, kst + (d * KS + kg) * TCH, vst + (d * KS + kg) * TCH,
                    vst + (pr * KS + kg) * TCH, load, math);
-        lds_barrier<2 * KS>();  // step σ + 1 is in LDS
+        lds_barrier<2 * KS * (SHD - 1)>();  // step σ + 1 is in LDS
       };
       unrolled<NSL>(iteration);
     }
@@ -563,27 +566,34 @@ template <typename T>
 hipError_t launch_prefill_t(PrefillParams P, int D, int maxq, const Launch& L) {
   const int64_t pairs = (int64_t)P.S * P.Hkv;
   auto tiles = [&](int rows) { const int qt = rows / P.G; return pairs * ((maxq + qt - 1) / qt); };
-  constexpr size_t kTile = (size_t)2 * 16 * (128 / 8) * 16;  // one K or V tile: two blocks of 16 rows
+  constexpr size_t kTile = (size_t)16 * 16 * 16 * 2;  // one K or V tile: 32 rows of 128 dims or 16 of 256
+  // LDS: SHD + 2 slots of KS K and V tiles, or the key groups' merge records
+  // (NW / KS waves x (NTW (NACC + 1) + 1) x 64 lanes x 16 bytes), whichever
+  // is larger.
+  auto lds = [&](int shd, int ks, int nw, int ntw, int nacc) {
+    const size_t slots = (size_t)(shd + 2) * ks * 2 * kTile;
+    const size_t merge = ks > 1 ? (size_t)(ks - 1) * (nw / ks) * (ntw * (nacc + 1) + 1) * 64 * 16 : 0;
+    return std::max(slots, merge);
+  };
   if (D == 128) {
     if (tiles(128) <= kPrefillSmallGrid) {
-      constexpr int NW = 8, NTW = 2, TB = 2, KS = 2;
+      constexpr int NW = 8, NTW = 2, TB = 2, SHD = 2, KS = 2;
       P.QT = 128 / P.G;
-      const size_t merge = (size_t)(KS - 1) * (NW / KS) * (NTW * (8 + 1) + 1) * 64 * 16;
-      const size_t smem = std::max((size_t)4 * KS * 2 * kTile, merge);  // four slots of K and V
-      return launch_lds<pa_prefill_h16<T, 128, NW, NTW, TB, 2, KS>>(smem, dim3((unsigned)tiles(128)),
-                                                                           dim3(NW * 64), smem, L, P);
+      const size_t smem = lds(SHD, KS, NW, NTW, 8);
+      return launch_lds<pa_prefill_h16<T, 128, NW, NTW, TB, SHD, KS>>(smem, dim3((unsigned)tiles(128)),
+                                                                       dim3(NW * 64), smem, L, P);
     }
-    constexpr int NW = 8, NTW = 2, TB = 2;
+    constexpr int NW = 8, NTW = 2, TB = 2, SHD = 2, KS = 1;
     P.QT = 256 / P.G;
-    return launch(pa_prefill_h16<T, 128, NW, NTW, TB, 2, 1>, dim3((unsigned)tiles(256)), dim3(NW * 64),
-                  4 * 2 * kTile, L, P);
+    const size_t smem = lds(SHD, KS, NW, NTW, 8);
+    return launch_lds<pa_prefill_h16<T, 128, NW, NTW, TB, SHD, KS>>(smem, dim3((unsigned)tiles(256)),
+                                                                     dim3(NW * 64), smem, L, P);
   }
-  constexpr int NW = 8, NTW = 1, TB = 1, KS = 2;
+  constexpr int NW = 8, NTW = 1, TB = 1, SHD = 2, KS = 2;
   P.QT = 64 / P.G;
-  const size_t merge = (size_t)(KS - 1) * (NW / KS) * (NTW * (16 + 1) + 1) * 64 * 16;
-  const size_t smem = std::max((size_t)4 * KS * 2 * kTile, merge);  // four slots of K and V
-  return launch_lds<pa_prefill_h16<T, 256, NW, NTW, TB, 2, KS>>(smem, dim3((unsigned)tiles(64)), dim3(NW * 64),
-                                                                       smem, L, P);
+  const size_t smem = lds(SHD, KS, NW, NTW, 16);
+  return launch_lds<pa_prefill_h16<T, 256, NW, NTW, TB, SHD, KS>>(smem, dim3((unsigned)tiles(64)), dim3(NW * 64),
+                                                                   smem, L, P);
 }
 
 int check_prefill(const void* out, const void* q, const void* k, const void* v, const int32_t* bt,
