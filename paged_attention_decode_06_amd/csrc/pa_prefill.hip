@@ -36,19 +36,23 @@ namespace {
 // v_permlane16_swap a, b exchanges rows 1/3 of a with rows 0/2 of b; with b a
 // copy of a, lane l then holds v[l] and v[l^16] across a and b, and
 // v_permlane32_swap pairs l with l^32 the same way. The max of a and b is
-// then the same value in both lanes of a pair.
+// then the same value in both lanes of a pair. The maxima are taken inside
+// the assembly too: the inputs are MFMA results or -inf, never signalling
+// NaNs, so they need none of the canonicalizing moves the compiler puts
+// around a max of values it cannot see the origin of.
 // Written as inline assembly with both registers read-write: the compiler's
 // builtin for these swaps returned the first result in place of the second
 // when both inputs held the same value. The s_nop pairs cover the VALU ->
 // lane-swap -> VALU data hazards.
 __device__ __forceinline__ float rows_max(float x) {
-  uint32_t a = __builtin_bit_cast(uint32_t, x), b = a;
-  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-  x = fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
-  a = __builtin_bit_cast(uint32_t, x);
-  b = a;
-  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
-  return fmaxf(__builtin_bit_cast(float, a), __builtin_bit_cast(float, b));
+  float t;
+  asm volatile(
+      "v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1\n\t"
+      "v_max_f32 %0, %0, %1\n\t"
+      "v_mov_b32 %1, %0\n\ts_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1\n\t"
+      "v_max_f32 %0, %0, %1"
+      : "+v"(x), "=&v"(t));
+  return x;
 }
 
 // gfx950 LDS transpose read of 16-bit data. Within each group of 16 lanes,
