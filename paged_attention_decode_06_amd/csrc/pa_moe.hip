@@ -44,7 +44,6 @@ __device__ __forceinline__ int clampi(int v, int lo, int hi) { return v < lo ? l
 // permute's scattered row writes slower (126 against 90 us, same workload).
 __device__ __forceinline__ u32x4 ld_rows(const void* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-  return *reinterpret_cast<const u32x4*>(p);
 }
 
 // ---------------------------------------------------------------- top-k softmax
