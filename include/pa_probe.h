@@ -1,8 +1,8 @@
 /*
  * pa_probe.h — measurement kernels beside the decode path (not part of it).
  *
- * They give the floors against which the decode kernels are judged on this
- * GPU: what one kernel launch costs when it does nothing, and how fast the
+ * They give the floors against which the decode kernels are measured on
+ * this GPU: what one kernel launch costs when it does nothing, and how fast the
  * bytes the decode must read (K and V of every context token, per KV head, in
  * the block order of the tables) can be read when nothing else is done with
  * them. The decode reads exactly these bytes (the roofline of the
