@@ -114,6 +114,93 @@ struct PrefillParams {
   float scale2;
 };
 
+// Reduction over the wave with DPP moves: shifts by 1, 2, 4 and 8 lanes
+// within each row of 16 leave the row's result in its lane 15, then the
+// row broadcasts (lane 15 into rows 1 and 3, lane 31 into rows 2 and 3)
+// combine the rows in lane 63. Lanes without a source keep `id`.
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, uint32_t id, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)id, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+  return wave_reduce(v, 0u, [](uint32_t a, uint32_t b) { return a + b; });
+}
+
+// Work item (sequence s, query tile t) of rank g when the items are ordered
+// by decreasing cost, ties by increasing s; s = -1 past the last item. The
+// cost of an item is the number of keys its last row sees, L - Q + min((t +
+// 1) QT, Q), which grows with t within a sequence. One sequence per lane (S
+// <= 64). Keys are shifted by T so that none is negative (a chunk longer
+// than its sequence has tiles that see no key). F(c), the number of items
+// with key >= c, has a closed form per sequence and is summed over the wave;
+// the rank-g key is the largest c with F(c) > g, found by bisection, and
+// each sequence has at most one item of that key.
+struct WorkItem {
+  int s, t;
+};
+
+__device__ WorkItem item_by_cost(const PrefillParams& P, int g, int nq, int lane) {
+  uint32_t base = 0, Q = 0;
+  int n = 0;
+  if (lane < P.S) {
+    int qb = P.qsl[lane], qe = P.qsl[lane + 1];
+    qb = min(max(qb, 0), P.T);
+    qe = min(max(qe, qb), P.T);
+    const int L = min(max(P.sl[lane], 0), P.MB * kBS);
+    const uint32_t Qall = (uint32_t)(qe - qb);
+    base = (uint32_t)L + ((uint32_t)P.T - Qall);  // key of the chunk's position 0, shifted by T
+    Q = min(Qall, (uint32_t)nq * (uint32_t)P.QT);  // tiles past the grid's nq are not computed
+    n = (int)((Q + P.QT - 1) / (uint32_t)P.QT);
+  }
+  const uint32_t QT = (uint32_t)P.QT, last = base + Q;  // last: the key of the sequence's last tile
+  auto count = [&](uint32_t c) -> uint32_t {            // this sequence's items with key >= c
+    if (n == 0 || c > last) return 0u;
+    const uint32_t m = ((c > base ? c - base : 0u) + QT - 1) / QT;  // first tile t + 1 whose key is >= c
+    return (uint32_t)n + 1u - max(m, 1u);
+  };
+  // Every sequence alike (a batch of equal prompts): rank g is tile n - 1 -
+  // g / S of sequence g % S, with no search.
+  const uint32_t b0 = __builtin_amdgcn_readfirstlane(base), q0 = __builtin_amdgcn_readfirstlane(Q);
+  if (__ballot(lane < P.S && (base != b0 || Q != q0)) == 0) {
+    const int n0 = __builtin_amdgcn_readfirstlane(n);
+    if (g >= n0 * P.S) return {-1, 0};
+    return {g % P.S, n0 - 1 - g / P.S};
+  }
+  const uint32_t total = wave_sum((uint32_t)n);
+  if ((uint32_t)g >= total) return {-1, 0};
+  // Bounds: F(lo) = total > g and F(hi) = 0 <= g.
+  uint32_t lo = wave_reduce(n ? base + min(QT, Q) : ~0u, ~0u, [](uint32_t a, uint32_t b) { return min(a, b); });
+  uint32_t hi = wave_reduce(n ? last : 0u, 0u, [](uint32_t a, uint32_t b) { return max(a, b); }) + 1u;
+  uint32_t f_hi = 0;
+  while (hi - lo > 1u) {
+    const uint32_t mid = lo + ((hi - lo) >> 1);
+    const uint32_t f = wave_sum(count(mid));
+    if (f > (uint32_t)g) {
+      lo = mid;
+    } else {
+      hi = mid;
+      f_hi = f;
+    }
+  }
+  // The item is the (g - F(lo + 1))-th, in sequence order, of those with key lo.
+  const uint32_t j = (uint32_t)g - f_hi;
+  const bool has = count(lo) != count(lo + 1u);
+  const uint64_t hm = __ballot(has);
+  const uint32_t below = (uint32_t)__builtin_popcountll(hm & ((1ull << lane) - 1ull));
+  const uint64_t pick = __ballot(has && below == j);
+  if (pick == 0) return {-1, 0};  // unreachable: F counts exactly the items above
+  const int sel = __builtin_ctzll(pick);
+  const uint32_t sb = __builtin_amdgcn_readlane(base, sel), sl = __builtin_amdgcn_readlane(last, sel);
+  const int sn = __builtin_amdgcn_readlane(n, sel);
+  return {sel, lo == sl ? sn - 1 : (int)((lo - sb) / QT) - 1};
+}
+
 template <typename T, int D, int NW, int NTW, int TB, int SHD, int KS>
 __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   typedef typename H16<T>::x8 tx8;
@@ -131,16 +218,31 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   constexpr int NWR = NW / KS;  // waves per key group (row groups)
   const int rg = w % NWR, kg = w / NWR;
 
+  // Launch order. The CUs take workgroups in launch order as they free up,
+  // so the order is the schedule: the items that see the most keys go first
+  // and the short ones fill the tail. With up to 64 sequences workgroup b
+  // takes KV head b % Hkv of the item of rank b / Hkv by cost (item_by_cost:
+  // exact, whatever the prefix and chunk lengths). With more, round r =
+  // b / pairs takes query tile nq - 1 - r of every (sequence, KV head) pair
+  // (the later tiles of a chunk see the most keys), the pairs rotated by r:
+  // workgroups go to the XCDs round-robin, and without the rotation each XCD
+  // would take the same few pairs in every round.
   const int pairs = P.S * P.Hkv;
-  // Launch order: round r = blockIdx / pairs takes query tile nq - 1 - r of
-  // every (sequence, KV head) pair, so the later tiles of each chunk, which
-  // see the most keys, start first and the short ones fill the tail. Within
-  // a round the pairs are rotated by r: workgroups go to the XCDs round-robin,
-  // and without the rotation each XCD would take the same few pairs in every
-  // round (all the tiles of the longest sequences on one XCD).
-  const int nq = (int)(gridDim.x / pairs), r = (int)(blockIdx.x / pairs);
-  const int pair = ((int)(blockIdx.x % pairs) + r) % pairs, qt = nq - 1 - r;
-  const int s = pair / P.Hkv, kvh = pair % P.Hkv;
+  const int nq = (int)(gridDim.x / pairs);
+  int s, kvh, qt;
+  if (P.S <= 64) {
+    const WorkItem it = item_by_cost(P, (int)(blockIdx.x / P.Hkv), nq, lane);
+    if (it.s < 0) return;
+    s = it.s;
+    qt = it.t;
+    kvh = (int)(blockIdx.x % P.Hkv);
+  } else {
+    const int r = (int)(blockIdx.x / pairs);
+    const int pair = ((int)(blockIdx.x % pairs) + r) % pairs;
+    qt = nq - 1 - r;
+    s = pair / P.Hkv;
+    kvh = pair % P.Hkv;
+  }
   // Extents, clamped so that no data value can send a read out of bounds.
   int qb = P.qsl[s], qe = P.qsl[s + 1];
   qb = min(max(qb, 0), P.T);

@@ -249,3 +249,38 @@ def test_prefill_large_grid_negative_scale(dev):
     x = dataclasses.replace(x, scale=-x.scale)
     say(f"prefill large grid, negative scale: {x.num_query_tokens} tokens")
     check_all(x, run(x, dev), "large grid, scale < 0")
+
+
+def test_prefill_many_sequences_round_order(dev):
+    """More than 64 sequences (the launch order by query-tile rounds), every token."""
+    rng = np.random.default_rng(63)
+    S = 80
+    x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=63, context_lens=rng.integers(0, 400, size=S),
+                              query_lens=rng.integers(1, 60, size=S))
+    say(f"prefill {S} sequences: {x.num_query_tokens} tokens")
+    check_all(x, run(x, dev), f"{S} sequences")
+
+
+@pytest.mark.parametrize("S", [5, 70])
+def test_prefill_tokens_past_max_query_len_not_computed(dev, S):
+    """max_query_len = 64 below the longest chunk: chunk tokens 0..63 of every
+    sequence are right, the later ones keep what the output held (64 is a whole
+    number of query tiles in every launch shape at G = 8). Both launch orders
+    (by cost up to 64 sequences, by rounds above)."""
+    rng = np.random.default_rng(64 + S)
+    ql = rng.integers(1, 200, size=S)
+    ql[0] = 199
+    x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=64 + S, context_lens=rng.integers(0, 600, size=S),
+                              query_lens=ql)
+    out = W.from_device(run(x, dev, max_query_len=64))
+    ref = oracle.attend_prefill(x.q, x.k_cache, x.v_cache, x.block_tables, x.seq_lens, x.query_start_loc,
+                                x.scale, x.cfg.dtype)
+    qsl = x.query_start_loc
+    inside = np.zeros(x.num_query_tokens, dtype=bool)
+    for s in range(S):
+        inside[qsl[s]:min(qsl[s + 1], qsl[s] + 64)] = True
+    err = max_err(out[inside], ref[inside])
+    say(f"  max_query_len 64, {S} seqs: max|err| = {err:.3e} over {int(inside.sum())} tokens, "
+        f"{int((~inside).sum())} past it")
+    assert err <= TOL[x.cfg.dtype]
+    assert np.isnan(out[~inside]).all()
