@@ -101,6 +101,9 @@ __device__ __forceinline__ void lds_barrier() {
   asm volatile("s_barrier" ::: "memory");
 }
 
+// Most 16-byte loads one lane makes per K (or V) tile in any launch shape.
+constexpr int kMaxLoadsPerTile = 2;
+
 struct PrefillParams {
   const void* q;
   const void* k;
@@ -215,6 +218,12 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   // Key split: the waves form KS groups of NW / KS; wave w takes row group
   // w % (NW / KS) and, of every KS consecutive key tiles, tile w / (NW / KS).
   static_assert(NW % KS == 0, "key groups of equal size");
+  // Loads per lane into LDS: K and V tiles of TB blocks of 16 rows of D / 8
+  // 16-byte chunks, spread over the NW x 64 lanes (NLD per tile each), KS
+  // tiles per step.
+  constexpr int NLD = TB * 16 * (D / 8) / (NW * 64);
+  static_assert(NLD >= 1 && NLD <= kMaxLoadsPerTile && NLD * NW * 64 == TB * 16 * (D / 8), "whole loads per tile");
+  constexpr int kLoadsPerStep = 2 * KS * NLD;
   constexpr int NWR = NW / KS;  // waves per key group (row groups)
   const int rg = w % NWR, kg = w / NWR;
 
@@ -426,9 +435,8 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     // keys, 16x16x32 P.V products) and one block at head_dim 256 (16 keys,
     // 16x16x16 P.V products): 8 KB of K and 8 KB of V either way.
     static_assert(KCH == 16 || KCH == 32, "head_dim 128 or 256");
-    static_assert(NW * 64 == TB * 16 * KCH, "per tile, one K and one V chunk per lane");
     constexpr int TCH = TB * 16 * KCH;               // chunks per K (or V) tile
-    constexpr int RPW = 64 / KCH;                    // tile rows one wave loads
+    constexpr int RPW = 64 / KCH;                    // tile rows one load of a wave covers
     using PV = std::conditional_t<TB == 2, tx8, tx4>;  // P as the B operand of a P.V product
     // LDS: NSL slots (step % NSL) of KS tiles each, K [NSL][KS][TB*16][KCH]
     // then V [NSL][KS][TB*16][KCH]. A step is KS consecutive key tiles, one
@@ -440,51 +448,64 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     constexpr int NSL = SHD + 2;
     u32x4* kst = reinterpret_cast<u32x4*>(smem);
     u32x4* vst = kst + NSL * KS * TCH;
-    // Loads: wave w takes tile rows w RPW .. w RPW + RPW - 1 of each tile of
-    // a step (all in one block), from K and from V. Its block is one
-    // block-table entry, read by a scalar load one step ahead; the buffer
-    // resources are zero bytes long for blocks past the end and V rows at
-    // or past kmax read past the block, so those arrive as zeros. Every wave
-    // issues the same 2 KS loads per step; a step's loads are waited for
-    // (vmcnt, counted by hand: the compiler does not track writes to LDS
-    // that come from loads) at the end of the iteration before its math.
+    // Loads: load i of wave w takes tile rows (i NW + w) RPW .. + RPW - 1 of
+    // each tile of a step (all in one block), from K and from V. Its block
+    // is one block-table entry, read by a scalar load one step ahead; the
+    // buffer resources are zero bytes long for blocks past the end and V
+    // rows at or past kmax read past the block, so those arrive as zeros.
+    // Every wave issues the same 2 KS NLD loads per step; a step's loads are
+    // waited for (vmcnt, counted by hand: the compiler does not track writes
+    // to LDS that come from loads) at the end of the iteration before its
+    // math.
     constexpr uint32_t kBlockBytes = (uint32_t)(kBS * D * sizeof(T));
-    const int wrow0 = w * RPW;                        // first tile row this wave writes
-    const int bw = wrow0 / 16;                        // this wave's block within a tile
-    const int lrow = (wrow0 + lane / KCH) % 16, lp = lane % KCH;  // row in the block, LDS position in the row
-    const int koff = (lrow * D + (lp ^ lrow) * 8) * (int)sizeof(T);
-    const int voff = (lrow * D + (lp ^ (2 * (lrow & 7))) * 8) * (int)sizeof(T);
+    const int lp = lane % KCH;                        // LDS position in the row
+    int wrow[kMaxLoadsPerTile], bw[kMaxLoadsPerTile], lrow[kMaxLoadsPerTile], koff[kMaxLoadsPerTile],
+        voff[kMaxLoadsPerTile];                       // per load i < NLD
+#pragma unroll
+    for (int i = 0; i < NLD; ++i) {
+      wrow[i] = (i * NW + w) * RPW;                   // first tile row load i writes
+      bw[i] = wrow[i] / 16;                           // its block within the tile
+      lrow[i] = (wrow[i] + lane / KCH) % 16;          // this lane's row in the block
+      koff[i] = (lrow[i] * D + (lp ^ lrow[i]) * 8) * (int)sizeof(T);
+      voff[i] = (lrow[i] * D + (lp ^ (2 * (lrow[i] & 7))) * 8) * (int)sizeof(T);
+    }
     // The block table through the constant address space: a uniform load
     // from there is a scalar load, waited for by the barrier's counter
     // rather than behind the vector loads in flight.
     const __attribute__((address_space(4))) int32_t* bt_const =
         (const __attribute__((address_space(4))) int32_t*)(uintptr_t)bt_row;
-    auto block_id = [&](int u) {                      // physical block of this wave's block of tile u
-      const int blk = __builtin_amdgcn_readfirstlane(min(u * TB + bw, nblk - 1));
+    auto block_id = [&](int u, int i) {               // physical block of load i's block of tile u
+      const int blk = __builtin_amdgcn_readfirstlane(min(u * TB + bw[i], nblk - 1));
       int id = bt_const[blk];
       if ((uint64_t)(int64_t)id >= (uint64_t)P.NB) id = 0;  // out-of-range ids read block 0
       return id;
     };
-    int id_next[KS];
+    int id_next[KS][NLD];
 #pragma unroll
-    for (int j = 0; j < KS; ++j) id_next[j] = block_id(j);
+    for (int j = 0; j < KS; ++j)
+#pragma unroll
+      for (int i = 0; i < NLD; ++i) id_next[j][i] = block_id(j, i);
     auto fetch = [&](int step, u32x4* k_next, u32x4* v_next) {  // the step's tiles into an LDS slot
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
         const int u = step * KS + j;
-        const int id = id_next[j];
-        id_next[j] = block_id(u + KS);
-        const int blk = u * TB + bw;
-        const bool ok = blk < nblk;
-        const int64_t off = ok ? (int64_t)id * block_elems : 0;
-        const uint32_t n = ok ? kBlockBytes : 0u;
-        const __amdgpu_buffer_rsrc_t kr = block_rsrc(kbase + off, n);
-        const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + off, n);
-        const int rows = j * TCH + wrow0 * KCH;
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(k_next + rows), 16,
-                                                 koff, 0, 0, 0);
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(v_next + rows), 16,
-                                                 blk * kBS + lrow < kmax ? voff : (int)kBlockBytes, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < NLD; ++i) {
+          const int id = id_next[j][i];
+          id_next[j][i] = block_id(u + KS, i);
+          const int blk = u * TB + bw[i];
+          const bool ok = blk < nblk;
+          const int64_t off = ok ? (int64_t)id * block_elems : 0;
+          const uint32_t n = ok ? kBlockBytes : 0u;
+          const __amdgpu_buffer_rsrc_t kr = block_rsrc(kbase + off, n);
+          const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + off, n);
+          const int rows = j * TCH + wrow[i] * KCH;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(k_next + rows),
+                                                   16, koff[i], 0, 0, 0);
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(v_next + rows),
+                                                   16, blk * kBS + lrow[i] < kmax ? voff[i] : (int)kBlockBytes,
+                                                   0, 0, 0);
+        }
       }
     };
     int klo[KK];                                      // lane offsets (chunks) of the K operand reads
@@ -572,7 +593,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
       };
       unrolled<SHD>(prologue);
     }
-    lds_barrier<2 * KS * (SHD - 1)>();  // step 0 is in LDS
+    lds_barrier<kLoadsPerStep * (SHD - 1)>();  // step 0 is in LDS
     PV pv[NTW];  // P of this wave's tile (late waves: applied one step later)
     for (int s0 = 0; s0 < niter; s0 += NSL) {
       auto iteration = [&](auto d_const) {
@@ -593,7 +614,7 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
         constexpr int nx = (d + SHD) % NSL, pr = (d + NSL - 1) % NSL;
         with_slots(kst + nx * KS * TCH, vst + nx * KS * TCH, kst + (d * KS + kg) * TCH, vst + (d * KS + kg) * TCH,
                    vst + (pr * KS + kg) * TCH, load, math);
-        lds_barrier<2 * KS * (SHD - 1)>();  // step σ + 1 is in LDS
+        lds_barrier<kLoadsPerStep * (SHD - 1)>();  // step σ + 1 is in LDS
       };
       unrolled<NSL>(iteration);
     }
@@ -661,45 +682,53 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
 //     tiles, so that 256 workgroups still fill the chip with 32-row waves;
 //   D = 128, larger grids: 256 rows per workgroup, 8 waves x 2 N-tiles, no
 //     key split;
-//   D = 256: 64 rows per workgroup, 4 row groups x 1 N-tile x 2 key groups
-//     of one-block tiles (the register budget of the wider rows, and twice
-//     the workgroups to even out sequences of different lengths).
-constexpr int kPrefillRows = 64;       // rows per workgroup of the smallest shape
+//   D = 256: 128 rows per workgroup, 8 waves x 1 N-tile (the register budget
+//     of the wider rows), two-block tiles, no key split (two-block tiles of
+//     256 dims in two key groups would need 256 KB of LDS). Two-block tiles
+//     make the P.V products 16x16x32 MFMAs; with one-block tiles they are
+//     16x16x16 ones, which do half the work in the same issue time (1.3x
+//     slower overall on the head_dim-256 batch).
+constexpr int kPrefillRows = 64;       // rows per workgroup: a lower bound over the launch shapes
 constexpr int kPrefillMaxNW = 8;       // waves per workgroup, largest launch shape
 constexpr int64_t kPrefillSmallGrid = 512;
 
+// A launch shape: D, NW waves, NTW N-tiles per wave, TB-block key tiles,
+// SHD steps in flight, KS key groups.
+template <int D_, int NW_, int NTW_, int TB_, int SHD_, int KS_>
+struct PShape {
+  static constexpr int D = D_, NW = NW_, NTW = NTW_, TB = TB_, SHD = SHD_, KS = KS_;
+};
+
+// Launches shape S: (NW / KS) x NTW x 16 query rows per workgroup, QT = rows
+// / G tokens (the last rows % G rows idle when G does not divide them). LDS:
+// SHD + 2 slots of KS K and V tiles, or the key groups' merge records (NW /
+// KS waves x (NTW (NACC + 1) + 1) x 64 lanes x 16 bytes), whichever is
+// larger.
+template <typename T, typename S>
+hipError_t launch_shape(PrefillParams P, int maxq, const Launch& L) {
+  constexpr int rows = S::NW / S::KS * S::NTW * 16;
+  static_assert(rows >= kPrefillRows && S::NW <= kPrefillMaxNW, "the grid bound check_prefill applies");
+  constexpr size_t tile = (size_t)S::TB * kBS * S::D * sizeof(T);  // one K or V tile
+  constexpr size_t slots = (size_t)(S::SHD + 2) * S::KS * 2 * tile;
+  constexpr size_t merge =
+      S::KS > 1 ? (size_t)(S::KS - 1) * (S::NW / S::KS) * (S::NTW * (S::D / 16 + 1) + 1) * 64 * 16 : 0;
+  constexpr size_t smem = slots > merge ? slots : merge;
+  static_assert(smem <= 160 * 1024, "LDS of one CU");
+  P.QT = rows / P.G;
+  const int64_t grid = (int64_t)P.S * P.Hkv * ((maxq + P.QT - 1) / P.QT);
+  return launch_lds<pa_prefill_h16<T, S::D, S::NW, S::NTW, S::TB, S::SHD, S::KS>>(
+      smem, dim3((unsigned)grid), dim3(S::NW * 64), smem, L, P);
+}
+
 template <typename T>
 hipError_t launch_prefill_t(PrefillParams P, int D, int maxq, const Launch& L) {
-  const int64_t pairs = (int64_t)P.S * P.Hkv;
-  auto tiles = [&](int rows) { const int qt = rows / P.G; return pairs * ((maxq + qt - 1) / qt); };
-  constexpr size_t kTile = (size_t)16 * 16 * 16 * 2;  // one K or V tile: 32 rows of 128 dims or 16 of 256
-  // LDS: SHD + 2 slots of KS K and V tiles, or the key groups' merge records
-  // (NW / KS waves x (NTW (NACC + 1) + 1) x 64 lanes x 16 bytes), whichever
-  // is larger.
-  auto lds = [&](int shd, int ks, int nw, int ntw, int nacc) {
-    const size_t slots = (size_t)(shd + 2) * ks * 2 * kTile;
-    const size_t merge = ks > 1 ? (size_t)(ks - 1) * (nw / ks) * (ntw * (nacc + 1) + 1) * 64 * 16 : 0;
-    return std::max(slots, merge);
-  };
   if (D == 128) {
-    if (tiles(128) <= kPrefillSmallGrid) {
-      constexpr int NW = 8, NTW = 2, TB = 2, SHD = 2, KS = 2;
-      P.QT = 128 / P.G;
-      const size_t smem = lds(SHD, KS, NW, NTW, 8);
-      return launch_lds<pa_prefill_h16<T, 128, NW, NTW, TB, SHD, KS>>(smem, dim3((unsigned)tiles(128)),
-                                                                       dim3(NW * 64), smem, L, P);
-    }
-    constexpr int NW = 8, NTW = 2, TB = 2, SHD = 2, KS = 1;
-    P.QT = 256 / P.G;
-    const size_t smem = lds(SHD, KS, NW, NTW, 8);
-    return launch_lds<pa_prefill_h16<T, 128, NW, NTW, TB, SHD, KS>>(smem, dim3((unsigned)tiles(256)),
-                                                                     dim3(NW * 64), smem, L, P);
+    const int qt = 128 / P.G;
+    if ((int64_t)P.S * P.Hkv * ((maxq + qt - 1) / qt) <= kPrefillSmallGrid)
+      return launch_shape<T, PShape<128, 8, 2, 2, 2, 2>>(P, maxq, L);
+    return launch_shape<T, PShape<128, 8, 2, 2, 2, 1>>(P, maxq, L);
   }
-  constexpr int NW = 8, NTW = 1, TB = 1, SHD = 2, KS = 2;
-  P.QT = 64 / P.G;
-  const size_t smem = lds(SHD, KS, NW, NTW, 16);
-  return launch_lds<pa_prefill_h16<T, 256, NW, NTW, TB, SHD, KS>>(smem, dim3((unsigned)tiles(64)), dim3(NW * 64),
-                                                                   smem, L, P);
+  return launch_shape<T, PShape<256, 8, 1, 2, 2, 1>>(P, maxq, L);
 }
 
 int check_prefill(const void* out, const void* q, const void* k, const void* v, const int32_t* bt,
