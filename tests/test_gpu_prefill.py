@@ -284,3 +284,38 @@ def test_prefill_tokens_past_max_query_len_not_computed(dev, S):
         f"{int((~inside).sum())} past it")
     assert err <= TOL[x.cfg.dtype]
     assert np.isnan(out[~inside]).all()
+
+
+def test_prefill_64_sequences_ranked_order(dev):
+    """64 sequences, the most that take the launch order ranked by cost, every token."""
+    rng = np.random.default_rng(66)
+    S = 64
+    x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=66, context_lens=rng.integers(0, 500, size=S),
+                              query_lens=rng.integers(1, 100, size=S))
+    say(f"prefill {S} sequences (ranked order): {x.num_query_tokens} tokens")
+    check_all(x, run(x, dev), f"{S} sequences")
+
+
+def test_prefill_mixed_batch_with_chunks_longer_than_their_sequence(dev):
+    """A mixed batch (ranked order, not the equal-sequence shortcut) in which two
+    chunks claim more tokens than their sequence holds: whole query tiles with
+    no visible key (zeros) rank below every other item and still run."""
+    cfg = W.PrefillConfig("neg-mixed", 6, 16, 2, 128, "bf16", ("custom",), ("custom",))
+    x = W.make_prefill_inputs(cfg, seed=67, context_lens=[0, 300, 0, 50, 1000, 0],
+                              query_lens=[40, 20, 30, 70, 5, 64])
+    claim = {0: 100, 2: 40}  # extra query tokens at negative positions, before the chunk's own
+    rows, qsl, ql = [], [0], []
+    for s in range(cfg.num_seqs):
+        extra = claim.get(s, 0)
+        if extra:
+            rows.append(W.make_prefill_inputs(cfg, seed=68 + s, context_lens=[0] * 6, query_lens=[extra] * 6)
+                        .q[:extra])
+        rows.append(x.q[x.query_start_loc[s]:x.query_start_loc[s + 1]])
+        ql.append(int(x.query_lens[s]) + extra)
+        qsl.append(qsl[-1] + ql[-1])
+    x.q = np.concatenate(rows)
+    x.query_lens = np.array(ql, dtype=np.int32)
+    x.query_start_loc = np.array(qsl, dtype=np.int32)
+    say(f"prefill mixed batch, chunks longer than their sequence: {x.num_query_tokens} tokens")
+    got = check_all(x, run(x, dev), "negative positions, mixed batch")
+    assert (got[0:100] == 0).all() and (got[qsl[2]:qsl[2] + 40] == 0).all()
