@@ -409,12 +409,12 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
       }
     }
   };
-  auto pack_p2 = [&](const T (&pb)[TB][4]) {  // two-block P as one B operand, in key order 4grp+i, 16+4grp+i
+  auto pack_p2 = [&](const T (&p0)[4], const T (&p1)[4]) {  // two blocks of P as one B operand, keys 4grp+i, 16+4grp+i
     tx8 pv;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      pv[i] = pb[0][i];
-      pv[4 + i] = pb[TB - 1][i];
+      pv[i] = p0[i];
+      pv[4 + i] = p1[i];
     }
     return pv;
   };
@@ -431,13 +431,17 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     // chunk c at c ^ 2 (r % 8) (the transpose read takes chunk pairs 2mt,
     // 2mt+1 from rows 4grp .. 4grp+3, and eight consecutive rows then hit
     // eight distinct 32-byte bank groups). Each lane loads the global chunk
-    // that its LDS position holds. A tile is two blocks at head_dim 128 (32
-    // keys, 16x16x32 P.V products) and one block at head_dim 256 (16 keys,
-    // 16x16x16 P.V products): 8 KB of K and 8 KB of V either way.
+    // that its LDS position holds. A tile is TB blocks of 16 keys; the P.V
+    // products take them in pairs (16x16x32 MFMAs), or one block at a time
+    // with TB = 1 (16x16x16 MFMAs, half the work in the same issue time).
     static_assert(KCH == 16 || KCH == 32, "head_dim 128 or 256");
     constexpr int TCH = TB * 16 * KCH;               // chunks per K (or V) tile
     constexpr int RPW = 64 / KCH;                    // tile rows one load of a wave covers
-    using PV = std::conditional_t<TB == 2, tx8, tx4>;  // P as the B operand of a P.V product
+    static_assert(TB == 1 || TB % 2 == 0, "one block, or pairs of blocks");
+    constexpr int NPB = TB == 1 ? 1 : TB / 2;        // P.V products per output tile and step
+    struct PV {                                       // P as the B operands of the P.V products
+      std::conditional_t<TB == 1, tx4, tx8> p[NPB];
+    };
     // LDS: NSL slots (step % NSL) of KS tiles each, K [NSL][KS][TB*16][KCH]
     // then V [NSL][KS][TB*16][KCH]. A step is KS consecutive key tiles, one
     // per key group. Steps σ + 1 .. σ + SHD load while step σ is computed,
@@ -533,41 +537,45 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
       for (int jj = 0; jj < NTW; ++jj) {
         T pb[TB][4];
         softmax_step(sc[jj], jj, u, pb);
-        if constexpr (TB == 2) {
-          pv[jj] = pack_p2(pb);
+        if constexpr (TB == 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pv[jj].p[0][i] = pb[0][i];
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) pv[jj][i] = pb[0][i];
+          for (int pp = 0; pp < NPB; ++pp) pv[jj].p[pp] = pack_p2(pb[2 * pp], pb[2 * pp + 1]);
         }
       }
     };
     // P.V products (and row sums) from the V tile at vt. V^T operand of
-    // M-tile mt (head dims 16mt .. 16mt+15): keys 4grp .. 4grp+3 of block 0
-    // (and the same of block 1 for two-block tiles), in the order the QK
-    // accumulator hands P over.
+    // M-tile mt (head dims 16mt .. 16mt+15) for the pair of blocks 2pp,
+    // 2pp + 1: keys 4grp .. 4grp+3 of each, in the order the QK accumulator
+    // hands P over (with TB = 1, those of block 0 alone).
     auto pv_apply = [&](const u32x4* vt, const PV (&pv)[NTW]) {
       const char* vb = reinterpret_cast<const char*>(vt);
-      PV vo[NACC];
 #pragma unroll
-      for (int mt = 0; mt < NACC; ++mt) {
-        const i16x4 lo = lds_read_tr16(vb + vlo[mt]);
-        if constexpr (TB == 2) {
-          const i16x4 hi = lds_read_tr16(vb + vlo[mt] + 16 * KCH * 16);
-          vo[mt] = __builtin_bit_cast(tx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-        } else {
-          vo[mt] = __builtin_bit_cast(tx4, lo);
+      for (int pp = 0; pp < NPB; ++pp) {
+        std::conditional_t<TB == 1, tx4, tx8> vo[NACC];
+#pragma unroll
+        for (int mt = 0; mt < NACC; ++mt) {
+          const i16x4 lo = lds_read_tr16(vb + vlo[mt] + 2 * pp * 16 * KCH * 16);
+          if constexpr (TB == 1) {
+            vo[mt] = __builtin_bit_cast(tx4, lo);
+          } else {
+            const i16x4 hi = lds_read_tr16(vb + vlo[mt] + (2 * pp + 1) * 16 * KCH * 16);
+            vo[mt] = __builtin_bit_cast(tx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
         }
-      }
 #pragma unroll
-      for (int jj = 0; jj < NTW; ++jj) {
-        if constexpr (TB == 2) {
+        for (int jj = 0; jj < NTW; ++jj) {
+          if constexpr (TB == 1) {
 #pragma unroll
-          for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma32(vo[mt], pv[jj], acc[jj][mt]);
-          accl[jj] = H16<T>::mma32(ones8, pv[jj], accl[jj]);
-        } else {
+            for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma16(vo[mt], pv[jj].p[0], acc[jj][mt]);
+            accl[jj] = H16<T>::mma16(ones4, pv[jj].p[0], accl[jj]);
+          } else {
 #pragma unroll
-          for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma16(vo[mt], pv[jj], acc[jj][mt]);
-          accl[jj] = H16<T>::mma16(ones4, pv[jj], accl[jj]);
+            for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma32(vo[mt], pv[jj].p[pp], acc[jj][mt]);
+            accl[jj] = H16<T>::mma32(ones8, pv[jj].p[pp], accl[jj]);
+          }
         }
       }
     };
@@ -681,7 +689,8 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
 //     few query tiles): 4 row groups x 2 N-tiles x 2 key groups of two-block
 //     tiles, so that 256 workgroups still fill the chip with 32-row waves;
 //   D = 128, larger grids: 256 rows per workgroup, 8 waves x 2 N-tiles, no
-//     key split;
+//     key split, four-block tiles (64 keys per step and barrier: 1.08-1.12x
+//     the two-block tiles on mixed batches and long contexts; 251 VGPRs);
 //   D = 256: 128 rows per workgroup, 8 waves x 1 N-tile (the register budget
 //     of the wider rows), two-block tiles, no key split (two-block tiles of
 //     256 dims in two key groups would need 256 KB of LDS). Two-block tiles
@@ -726,7 +735,7 @@ hipError_t launch_prefill_t(PrefillParams P, int D, int maxq, const Launch& L) {
     const int qt = 128 / P.G;
     if ((int64_t)P.S * P.Hkv * ((maxq + qt - 1) / qt) <= kPrefillSmallGrid)
       return launch_shape<T, PShape<128, 8, 2, 2, 2, 2>>(P, maxq, L);
-    return launch_shape<T, PShape<128, 8, 2, 2, 2, 1>>(P, maxq, L);
+    return launch_shape<T, PShape<128, 8, 2, 4, 2, 1>>(P, maxq, L);
   }
   return launch_shape<T, PShape<256, 8, 1, 2, 2, 1>>(P, maxq, L);
 }
