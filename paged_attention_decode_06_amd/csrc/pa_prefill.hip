@@ -84,9 +84,9 @@ __device__ __forceinline__ void unrolled(F& f) {
 template <typename Fetch, typename Math>
 __device__ __forceinline__ void with_slots(u32x4* __restrict__ k_next, u32x4* __restrict__ v_next,
                                            const u32x4* __restrict__ k_cur, const u32x4* __restrict__ v_cur,
-                                           const u32x4* __restrict__ v_prev, Fetch& fetch, Math& math) {
+                                           Fetch& fetch, Math& math) {
   fetch(k_next, v_next);
-  math(k_cur, v_cur, v_prev);
+  math(k_cur, v_cur);
 }
 
 // Workgroup barrier for LDS written by loads: waits until at most N loads
@@ -102,7 +102,7 @@ __device__ __forceinline__ void lds_barrier() {
 }
 
 // Most 16-byte loads one lane makes per K (or V) tile in any launch shape.
-constexpr int kMaxLoadsPerTile = 2;
+constexpr int kMaxLoadsPerTile = 4;
 
 struct PrefillParams {
   const void* q;
@@ -444,12 +444,11 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
     };
     // LDS: NSL slots (step % NSL) of KS tiles each, K [NSL][KS][TB*16][KCH]
     // then V [NSL][KS][TB*16][KCH]. A step is KS consecutive key tiles, one
-    // per key group. Steps σ + 1 .. σ + SHD load while step σ is computed,
-    // and half the waves read V of step σ - 1 during step σ (below): SHD + 2
-    // slots cover both, and the loop runs in groups of NSL so that every slot
+    // per key group. Steps σ + 1 .. σ + SHD load while step σ is computed:
+    // SHD + 1 slots, and the loop runs in groups of NSL so that every slot
     // index is a compile-time constant.
-    static_assert(SHD >= 2, "at least two steps in flight");
-    constexpr int NSL = SHD + 2;
+    static_assert(SHD >= 1, "a step in flight");
+    constexpr int NSL = SHD + 1;
     u32x4* kst = reinterpret_cast<u32x4*>(smem);
     u32x4* vst = kst + NSL * KS * TCH;
     // Loads: load i of wave w takes tile rows (i NW + w) RPW .. + RPW - 1 of
@@ -580,48 +579,38 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
       }
     };
     // Iteration σ (slot σ % NSL) starts the loads of step σ + SHD, runs this
-    // wave's share of the math, waits for the loads of step σ + 1 and ends
-    // with one barrier. Waves w < NW/2 run their tile of the step in order:
-    // QK products, softmax, P.V products. Their SIMD partners (w + NW/2)
-    // run the P.V products of their previous tile first, then the QK
-    // products and softmax of this one: while one wave of a SIMD has the
-    // matrix unit, the other mostly has the vector unit, where the same
-    // order in both would queue them on one unit at a time. The loop runs in
-    // whole groups of NSL; iterations past the last step load nothing, and
-    // one extra iteration lets the late waves finish.
+    // wave's tile of the step (QK products, softmax, P.V products), waits
+    // for the loads of step σ + 1 and ends with one barrier. The loop runs
+    // in whole groups of NSL; iterations past the last step load nothing.
     const int nsteps = (ntiles + KS - 1) / KS;
-    const int niter = nsteps + 1;
     {
-      auto none = [](const u32x4*, const u32x4*, const u32x4*) {};
+      auto none = [](const u32x4*, const u32x4*) {};
       auto prologue = [&](auto d_const) {
         constexpr int d = decltype(d_const)::value;
         auto f = [&](u32x4* kn, u32x4* vn) { fetch(d, kn, vn); };
-        with_slots(kst + d * KS * TCH, vst + d * KS * TCH, kst + SHD * KS * TCH, vst + SHD * KS * TCH,
-                   vst + (SHD + 1) * KS * TCH, f, none);
+        with_slots(kst + d * KS * TCH, vst + d * KS * TCH, kst + SHD * KS * TCH, vst + SHD * KS * TCH, f, none);
       };
       unrolled<SHD>(prologue);
     }
     lds_barrier<kLoadsPerStep * (SHD - 1)>();  // step 0 is in LDS
-    PV pv[NTW];  // P of this wave's tile (late waves: applied one step later)
-    for (int s0 = 0; s0 < niter; s0 += NSL) {
+    for (int s0 = 0; s0 < nsteps; s0 += NSL) {
       auto iteration = [&](auto d_const) {
         constexpr int d = decltype(d_const)::value;  // == step % NSL
         const int step = s0 + d;
         const int t = step * KS + kg;
-        const bool late = w >= NW / 2;
         auto load = [&](u32x4* kn, u32x4* vn) { fetch(step + SHD, kn, vn); };
-        auto math = [&](const u32x4* kc, const u32x4* vc, const u32x4* vp) {
-          if (late && step > 0 && t - KS < ntiles) pv_apply(vp, pv);
+        auto math = [&](const u32x4* kc, const u32x4* vc) {
           if (t < ntiles) {
             f32x4 sc[NTW][TB];
+            PV pv[NTW];
             qk_tile(kc, sc);
             softmax_pack(t, sc, pv);
-            if (!late) pv_apply(vc, pv);
+            pv_apply(vc, pv);
           }
         };
-        constexpr int nx = (d + SHD) % NSL, pr = (d + NSL - 1) % NSL;
+        constexpr int nx = (d + SHD) % NSL;
         with_slots(kst + nx * KS * TCH, vst + nx * KS * TCH, kst + (d * KS + kg) * TCH, vst + (d * KS + kg) * TCH,
-                   vst + (pr * KS + kg) * TCH, load, math);
+                   load, math);
         lds_barrier<kLoadsPerStep * (SHD - 1)>();  // step σ + 1 is in LDS
       };
       unrolled<NSL>(iteration);
@@ -682,21 +671,21 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
   }
 }
 
-// Prefill launch shapes (8 waves, two steps of K/V tiles in flight, measured
-// on the four prefill workloads against other wave, N-tile, tile, key-split
-// and prefetch choices):
+// Prefill launch shapes: 8 waves, four-block key tiles (64 keys per step and
+// barrier), one step of K/V tiles in flight (measured on the four prefill
+// workloads against other wave, N-tile, tile, key-split and prefetch
+// choices; 64-key steps with one step in flight beat 32-key steps with two
+// in every shape, 1.07-1.12x):
 //   D = 128, at most kPrefillSmallGrid workgroups of 128 rows (long contexts,
-//     few query tiles): 4 row groups x 2 N-tiles x 2 key groups of two-block
-//     tiles, so that 256 workgroups still fill the chip with 32-row waves;
+//     few query tiles): 4 row groups x 2 N-tiles x 2 key groups, so that 256
+//     workgroups still fill the chip with 32-row waves;
 //   D = 128, larger grids: 256 rows per workgroup, 8 waves x 2 N-tiles, no
-//     key split, four-block tiles (64 keys per step and barrier: 1.08-1.12x
-//     the two-block tiles on mixed batches and long contexts; 251 VGPRs);
+//     key split;
 //   D = 256: 128 rows per workgroup, 8 waves x 1 N-tile (the register budget
-//     of the wider rows), two-block tiles, no key split (two-block tiles of
-//     256 dims in two key groups would need 256 KB of LDS). Two-block tiles
-//     make the P.V products 16x16x32 MFMAs; with one-block tiles they are
-//     16x16x16 ones, which do half the work in the same issue time (1.3x
-//     slower overall on the head_dim-256 batch).
+//     of the wider rows), no key split.
+// The P.V products take a tile's blocks in pairs, as 16x16x32 MFMAs
+// (one-block tiles would make them 16x16x16 ones, which do half the work in
+// the same issue time).
 constexpr int kPrefillRows = 64;       // rows per workgroup: a lower bound over the launch shapes
 constexpr int kPrefillMaxNW = 8;       // waves per workgroup, largest launch shape
 constexpr int64_t kPrefillSmallGrid = 512;
@@ -710,7 +699,7 @@ struct PShape {
 
 // Launches shape S: (NW / KS) x NTW x 16 query rows per workgroup, QT = rows
 // / G tokens (the last rows % G rows idle when G does not divide them). LDS:
-// SHD + 2 slots of KS K and V tiles, or the key groups' merge records (NW /
+// SHD + 1 slots of KS K and V tiles, or the key groups' merge records (NW /
 // KS waves x (NTW (NACC + 1) + 1) x 64 lanes x 16 bytes), whichever is
 // larger.
 template <typename T, typename S>
@@ -718,7 +707,7 @@ hipError_t launch_shape(PrefillParams P, int maxq, const Launch& L) {
   constexpr int rows = S::NW / S::KS * S::NTW * 16;
   static_assert(rows >= kPrefillRows && S::NW <= kPrefillMaxNW, "the grid bound check_prefill applies");
   constexpr size_t tile = (size_t)S::TB * kBS * S::D * sizeof(T);  // one K or V tile
-  constexpr size_t slots = (size_t)(S::SHD + 2) * S::KS * 2 * tile;
+  constexpr size_t slots = (size_t)(S::SHD + 1) * S::KS * 2 * tile;
   constexpr size_t merge =
       S::KS > 1 ? (size_t)(S::KS - 1) * (S::NW / S::KS) * (S::NTW * (S::D / 16 + 1) + 1) * 64 * 16 : 0;
   constexpr size_t smem = slots > merge ? slots : merge;
@@ -734,10 +723,10 @@ hipError_t launch_prefill_t(PrefillParams P, int D, int maxq, const Launch& L) {
   if (D == 128) {
     const int qt = 128 / P.G;
     if ((int64_t)P.S * P.Hkv * ((maxq + qt - 1) / qt) <= kPrefillSmallGrid)
-      return launch_shape<T, PShape<128, 8, 2, 2, 2, 2>>(P, maxq, L);
-    return launch_shape<T, PShape<128, 8, 2, 4, 2, 1>>(P, maxq, L);
+      return launch_shape<T, PShape<128, 8, 2, 4, 1, 2>>(P, maxq, L);
+    return launch_shape<T, PShape<128, 8, 2, 4, 1, 1>>(P, maxq, L);
   }
-  return launch_shape<T, PShape<256, 8, 1, 2, 2, 1>>(P, maxq, L);
+  return launch_shape<T, PShape<256, 8, 1, 4, 1, 1>>(P, maxq, L);
 }
 
 int check_prefill(const void* out, const void* q, const void* k, const void* v, const int32_t* bt,
