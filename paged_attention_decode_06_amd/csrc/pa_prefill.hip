@@ -672,15 +672,15 @@ __global__ __launch_bounds__(NW * 64) void pa_prefill_h16(PrefillParams P) {
 }
 
 // Prefill launch shapes: 8 waves, four-block key tiles (64 keys per step and
-// barrier), one step of K/V tiles in flight (measured on the four prefill
-// workloads against other wave, N-tile, tile, key-split and prefetch
-// choices; 64-key steps with one step in flight beat 32-key steps with two
-// in every shape, 1.07-1.12x):
+// barrier), one step of K/V tiles in flight where the LDS holds only two
+// slots of them (measured on the four prefill workloads against other wave,
+// N-tile, tile, key-split and prefetch choices; 64-key steps with one step
+// in flight beat 32-key steps with two in every shape, 1.07-1.12x):
 //   D = 128, at most kPrefillSmallGrid workgroups of 128 rows (long contexts,
 //     few query tiles): 4 row groups x 2 N-tiles x 2 key groups, so that 256
 //     workgroups still fill the chip with 32-row waves;
 //   D = 128, larger grids: 256 rows per workgroup, 8 waves x 2 N-tiles, no
-//     key split;
+//     key split, two steps in flight (96 KB; 1.02x one step);
 //   D = 256: 128 rows per workgroup, 8 waves x 1 N-tile (the register budget
 //     of the wider rows), no key split.
 // The P.V products take a tile's blocks in pairs, as 16x16x32 MFMAs
@@ -724,7 +724,7 @@ hipError_t launch_prefill_t(PrefillParams P, int D, int maxq, const Launch& L) {
     const int qt = 128 / P.G;
     if ((int64_t)P.S * P.Hkv * ((maxq + qt - 1) / qt) <= kPrefillSmallGrid)
       return launch_shape<T, PShape<128, 8, 2, 4, 1, 2>>(P, maxq, L);
-    return launch_shape<T, PShape<128, 8, 2, 4, 1, 1>>(P, maxq, L);
+    return launch_shape<T, PShape<128, 8, 2, 4, 2, 1>>(P, maxq, L);
   }
   return launch_shape<T, PShape<256, 8, 1, 4, 1, 1>>(P, maxq, L);
 }
