@@ -206,24 +206,34 @@ def test_prefill_rejects_f32(dev):
         run(x, dev)
 
 
-def test_prefill_large_grid_every_token(dev):
-    """More than 512 workgroups (the many-workgroup launch shape), every token compared."""
+# Table widths for the many-workgroup tests: the natural one (at most 2048
+# tokens: the 4-wave short-table shape) and 160 blocks (2560 tokens: the
+# 8-wave shape).
+WIDE = [None, 160]
+
+
+@pytest.mark.parametrize("mb", WIDE)
+def test_prefill_large_grid_every_token(dev, mb):
+    """More than 512 workgroups (the many-workgroup launch shapes), every token compared."""
     rng = np.random.default_rng(58)
     S = 40
     ctx = rng.integers(0, 300, size=S)
     ql = rng.integers(100, 129, size=S)
-    x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=58, context_lens=ctx, query_lens=ql)
-    say(f"prefill large grid: {S} seqs, {x.num_query_tokens} tokens")
+    x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=58, context_lens=ctx, query_lens=ql,
+                              max_blocks_per_seq=mb)
+    say(f"prefill large grid: {S} seqs, {x.num_query_tokens} tokens, table width {x.max_blocks_per_seq}")
     check_all(x, run(x, dev), "large grid")
 
 
-def test_prefill_large_grid_odd_group(dev):
-    """The 256-row launch shape with G = 3 (85 tokens x 3 heads = 255 rows per tile), every token."""
+@pytest.mark.parametrize("mb", WIDE)
+def test_prefill_large_grid_odd_group(dev, mb):
+    """The many-workgroup shapes with G = 3 (42 tokens x 3 heads = 126 of 128
+    rows, or 85 x 3 = 255 of 256), every token."""
     rng = np.random.default_rng(59)
     S = 40
     cfg = W.PrefillConfig("g3", S, 12, 4, 128, "bf16", ("custom",), ("custom",))
     x = W.make_prefill_inputs(cfg, seed=59, context_lens=rng.integers(0, 200, size=S),
-                              query_lens=rng.integers(150, 201, size=S))
+                              query_lens=rng.integers(150, 201, size=S), max_blocks_per_seq=mb)
     say(f"prefill large grid, G=3: {x.num_query_tokens} tokens")
     check_all(x, run(x, dev), "large grid G=3")
 
@@ -240,23 +250,25 @@ def test_prefill_scale_sign_and_zero(dev, D, mult):
     check_all(x, run(x, dev), f"scale x{mult} D={D}")
 
 
-def test_prefill_large_grid_negative_scale(dev):
-    """The 256-row launch shape with a negative scale, every token."""
+@pytest.mark.parametrize("mb", WIDE)
+def test_prefill_large_grid_negative_scale(dev, mb):
+    """The many-workgroup shapes with a negative scale, every token."""
     rng = np.random.default_rng(62)
     S = 40
     x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=62, context_lens=rng.integers(0, 300, size=S),
-                              query_lens=rng.integers(100, 129, size=S))
+                              query_lens=rng.integers(100, 129, size=S), max_blocks_per_seq=mb)
     x = dataclasses.replace(x, scale=-x.scale)
     say(f"prefill large grid, negative scale: {x.num_query_tokens} tokens")
     check_all(x, run(x, dev), "large grid, scale < 0")
 
 
-def test_prefill_many_sequences_round_order(dev):
+@pytest.mark.parametrize("mb", WIDE)
+def test_prefill_many_sequences_round_order(dev, mb):
     """More than 64 sequences (the launch order by query-tile rounds), every token."""
     rng = np.random.default_rng(63)
     S = 80
     x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=63, context_lens=rng.integers(0, 400, size=S),
-                              query_lens=rng.integers(1, 60, size=S))
+                              query_lens=rng.integers(1, 60, size=S), max_blocks_per_seq=mb)
     say(f"prefill {S} sequences: {x.num_query_tokens} tokens")
     check_all(x, run(x, dev), f"{S} sequences")
 
@@ -286,12 +298,13 @@ def test_prefill_tokens_past_max_query_len_not_computed(dev, S):
     assert np.isnan(out[~inside]).all()
 
 
-def test_prefill_64_sequences_ranked_order(dev):
+@pytest.mark.parametrize("mb", WIDE)
+def test_prefill_64_sequences_ranked_order(dev, mb):
     """64 sequences, the most that take the launch order ranked by cost, every token."""
     rng = np.random.default_rng(66)
     S = 64
     x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=66, context_lens=rng.integers(0, 500, size=S),
-                              query_lens=rng.integers(1, 100, size=S))
+                              query_lens=rng.integers(1, 100, size=S), max_blocks_per_seq=mb)
     say(f"prefill {S} sequences (ranked order): {x.num_query_tokens} tokens")
     check_all(x, run(x, dev), f"{S} sequences")
 
