@@ -138,48 +138,90 @@ __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
 // Work item (sequence s, query tile t) of rank g when the items are ordered
 // by decreasing cost, ties by increasing s; s = -1 past the last item. The
 // cost of an item is the number of keys its last row sees, L - Q + min((t +
-// 1) QT, Q), which grows with t within a sequence. One sequence per lane (S
-// <= 64). Keys are shifted by T so that none is negative (a chunk longer
-// than its sequence has tiles that see no key). F(c), the number of items
-// with key >= c, has a closed form per sequence and is summed over the wave;
-// the rank-g key is the largest c with F(c) > g, found by bisection, and
-// each sequence has at most one item of that key.
+// 1) QT, Q), which grows with t within a sequence. Up to 64 SLOTS
+// sequences, sequence s in slot s / 64 of lane s % 64. Keys are shifted by T
+// so that none is negative (a chunk longer than its sequence has tiles that
+// see no key). F(c), the number of items with key >= c, has a closed form
+// per sequence and is summed over the slots and the wave; the rank-g key is
+// the largest c with F(c) > g, found by bisection, and each sequence has at
+// most one item of that key.
+constexpr int kRankedSeqs = 256;  // batches up to this size launch in ranked order (4 sequences per lane)
+
 struct WorkItem {
-  int s, t;
+  int s, t;  // s = -1: no item; s = -2: every sequence has the same prefix (take the round order)
 };
 
+template <int SLOTS>
 __device__ WorkItem item_by_cost(const PrefillParams& P, int g, int nq, int lane) {
-  uint32_t base = 0, Q = 0;
-  int n = 0;
-  if (lane < P.S) {
-    int qb = P.qsl[lane], qe = P.qsl[lane + 1];
-    qb = min(max(qb, 0), P.T);
-    qe = min(max(qe, qb), P.T);
-    const int L = min(max(P.sl[lane], 0), P.MB * kBS);
-    const uint32_t Qall = (uint32_t)(qe - qb);
-    base = (uint32_t)L + ((uint32_t)P.T - Qall);  // key of the chunk's position 0, shifted by T
-    Q = min(Qall, (uint32_t)nq * (uint32_t)P.QT);  // tiles past the grid's nq are not computed
-    n = (int)((Q + P.QT - 1) / (uint32_t)P.QT);
+  const int slots = SLOTS == 1 ? 1 : (P.S + 63) / 64;  // 1 .. SLOTS, wave-uniform
+  const uint32_t QT = (uint32_t)P.QT;
+  uint32_t base[SLOTS], Q[SLOTS], last[SLOTS];
+  int n[SLOTS];
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k) {
+    base[k] = Q[k] = 0u;
+    n[k] = 0;
+    const int sq = 64 * k + lane;
+    if (k < slots && sq < P.S) {
+      int qb = P.qsl[sq], qe = P.qsl[sq + 1];
+      qb = min(max(qb, 0), P.T);
+      qe = min(max(qe, qb), P.T);
+      const int L = min(max(P.sl[sq], 0), P.MB * kBS);
+      const uint32_t Qall = (uint32_t)(qe - qb);
+      base[k] = (uint32_t)L + ((uint32_t)P.T - Qall);  // key of the chunk's position 0, shifted by T
+      Q[k] = min(Qall, (uint32_t)nq * QT);             // tiles past the grid's nq are not computed
+      n[k] = (int)((Q[k] + QT - 1) / QT);
+    }
+    last[k] = base[k] + Q[k];  // the key of the sequence's last tile
   }
-  const uint32_t QT = (uint32_t)P.QT, last = base + Q;  // last: the key of the sequence's last tile
-  auto count = [&](uint32_t c) -> uint32_t {            // this sequence's items with key >= c
-    if (n == 0 || c > last) return 0u;
-    const uint32_t m = ((c > base ? c - base : 0u) + QT - 1) / QT;  // first tile t + 1 whose key is >= c
-    return (uint32_t)n + 1u - max(m, 1u);
+  auto count_one = [&](int k, uint32_t c) -> uint32_t {  // items of slot k's sequence with key >= c
+    if (n[k] == 0 || c > last[k]) return 0u;
+    const uint32_t m = ((c > base[k] ? c - base[k] : 0u) + QT - 1) / QT;  // first tile t + 1 whose key is >= c
+    return (uint32_t)n[k] + 1u - max(m, 1u);
+  };
+  auto count = [&](uint32_t c) -> uint32_t {  // this lane's items with key >= c
+    uint32_t f = 0;
+#pragma unroll
+    for (int k = 0; k < SLOTS; ++k)
+      if (k < slots) f += count_one(k, c);
+    return f;
   };
   // Every sequence alike (a batch of equal prompts): rank g is tile n - 1 -
-  // g / S of sequence g % S, with no search.
-  const uint32_t b0 = __builtin_amdgcn_readfirstlane(base), q0 = __builtin_amdgcn_readfirstlane(Q);
-  if (__ballot(lane < P.S && (base != b0 || Q != q0)) == 0) {
-    const int n0 = __builtin_amdgcn_readfirstlane(n);
-    if (g >= n0 * P.S) return {-1, 0};
-    return {g % P.S, n0 - 1 - g / P.S};
+  // g / S of sequence g % S, with no search. Above 64 sequences, every
+  // sequence with the same prefix but chunks of different lengths (fresh
+  // prompts): an item's cost is then its tile's end, so the order by
+  // query-tile rounds is this order already and spares the search (which
+  // up to 64 sequences costs about what the round order would lose).
+  const uint32_t b0 = __builtin_amdgcn_readfirstlane(base[0]), q0 = __builtin_amdgcn_readfirstlane(Q[0]);
+  bool base_differs = false, q_differs = false;
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k)
+    if (k < slots && 64 * k + lane < P.S) {
+      base_differs |= base[k] != b0;
+      q_differs |= Q[k] != q0;
+    }
+  if (__ballot(base_differs) == 0) {
+    const bool chunks_differ = __ballot(q_differs) != 0;
+    if (SLOTS > 1 && chunks_differ) return {-2, 0};
+    if (!chunks_differ) {
+      const int n0 = __builtin_amdgcn_readfirstlane(n[0]);
+      if (g >= n0 * P.S) return {-1, 0};
+      return {g % P.S, n0 - 1 - g / P.S};
+    }
   }
-  const uint32_t total = wave_sum((uint32_t)n);
+  uint32_t nsum = 0, lo_l = ~0u, hi_l = 0u;
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k)
+    if (k < slots && n[k]) {
+      nsum += (uint32_t)n[k];
+      lo_l = min(lo_l, base[k] + min(QT, Q[k]));
+      hi_l = max(hi_l, last[k]);
+    }
+  const uint32_t total = wave_sum(nsum);
   if ((uint32_t)g >= total) return {-1, 0};
   // Bounds: F(lo) = total > g and F(hi) = 0 <= g.
-  uint32_t lo = wave_reduce(n ? base + min(QT, Q) : ~0u, ~0u, [](uint32_t a, uint32_t b) { return min(a, b); });
-  uint32_t hi = wave_reduce(n ? last : 0u, 0u, [](uint32_t a, uint32_t b) { return max(a, b); }) + 1u;
+  uint32_t lo = wave_reduce(lo_l, ~0u, [](uint32_t a, uint32_t b) { return min(a, b); });
+  uint32_t hi = wave_reduce(hi_l, 0u, [](uint32_t a, uint32_t b) { return max(a, b); }) + 1u;
   uint32_t f_hi = 0;
   while (hi - lo > 1u) {
     const uint32_t mid = lo + ((hi - lo) >> 1);
@@ -191,17 +233,25 @@ __device__ WorkItem item_by_cost(const PrefillParams& P, int g, int nq, int lane
       f_hi = f;
     }
   }
-  // The item is the (g - F(lo + 1))-th, in sequence order, of those with key lo.
-  const uint32_t j = (uint32_t)g - f_hi;
-  const bool has = count(lo) != count(lo + 1u);
-  const uint64_t hm = __ballot(has);
-  const uint32_t below = (uint32_t)__builtin_popcountll(hm & ((1ull << lane) - 1ull));
-  const uint64_t pick = __ballot(has && below == j);
-  if (pick == 0) return {-1, 0};  // unreachable: F counts exactly the items above
-  const int sel = __builtin_ctzll(pick);
-  const uint32_t sb = __builtin_amdgcn_readlane(base, sel), sl = __builtin_amdgcn_readlane(last, sel);
-  const int sn = __builtin_amdgcn_readlane(n, sel);
-  return {sel, lo == sl ? sn - 1 : (int)((lo - sb) / QT) - 1};
+  // The item is the (g - F(lo + 1))-th, in sequence order (slot by slot,
+  // lane by lane), of those with key lo.
+  uint32_t j = (uint32_t)g - f_hi;
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k) {
+    if (k >= slots) break;
+    const bool has = count_one(k, lo) != count_one(k, lo + 1u);
+    const uint64_t hm = __ballot(has);
+    const uint32_t cnt = (uint32_t)__builtin_popcountll(hm);
+    if (j < cnt) {
+      const uint32_t below = (uint32_t)__builtin_popcountll(hm & ((1ull << lane) - 1ull));
+      const int sel = __builtin_ctzll(__ballot(has && below == j));
+      const uint32_t sb = __builtin_amdgcn_readlane(base[k], sel), sl = __builtin_amdgcn_readlane(last[k], sel);
+      const int sn = __builtin_amdgcn_readlane(n[k], sel);
+      return {64 * k + sel, lo == sl ? sn - 1 : (int)((lo - sb) / QT) - 1};
+    }
+    j -= cnt;
+  }
+  return {-1, 0};  // unreachable: F counts exactly the items above
 }
 
 template <typename T, int D, int NW, int NTW, int TB, int SHD, int KS>
@@ -227,21 +277,25 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
   constexpr int NWR = NW / KS;  // waves per key group (row groups)
   const int rg = w % NWR, kg = w / NWR;
 
-  // Launch order. The CUs take workgroups in launch order as they free up,
-  // so the order is the schedule: the items that see the most keys go first
-  // and the short ones fill the tail. With up to 64 sequences workgroup b
-  // takes KV head b % Hkv of the item of rank b / Hkv by cost (item_by_cost:
-  // exact, whatever the prefix and chunk lengths). With more, round r =
-  // b / pairs takes query tile nq - 1 - r of every (sequence, KV head) pair
-  // (the later tiles of a chunk see the most keys), the pairs rotated by r:
-  // workgroups go to the XCDs round-robin, and without the rotation each XCD
-  // would take the same few pairs in every round.
+  // Launch order. The CUs take workgroups in launch order as they free up, so
+  // the order is the schedule: the items that see the most keys go first and
+  // the short ones fill the tail. With up to kRankedSeqs sequences (above 64,
+  // only when their prefix lengths differ), workgroup b takes KV head b % Hkv
+  // of the item of rank b / Hkv by cost (item_by_cost: exact, whatever the
+  // prefix and chunk lengths). Otherwise round r = b / pairs takes query tile
+  // nq - 1 - r of every (sequence, KV head) pair (the later tiles of a chunk
+  // see the most keys; with equal prefixes that is the order by cost), the
+  // pairs rotated by r: workgroups go to the XCDs round-robin, and without the
+  // rotation each XCD would take the same few pairs in every round.
   const int pairs = P.S * P.Hkv;
   const int nq = (int)(gridDim.x / pairs);
   int s, kvh, qt;
-  if (P.S <= 64) {
-    const WorkItem it = item_by_cost(P, (int)(blockIdx.x / P.Hkv), nq, lane);
-    if (it.s < 0) return;
+  const int rank = (int)(blockIdx.x / P.Hkv);
+  const WorkItem it = P.S <= 64            ? item_by_cost<1>(P, rank, nq, lane)
+                      : P.S <= kRankedSeqs ? item_by_cost<4>(P, rank, nq, lane)
+                                           : WorkItem{-2, 0};
+  if (it.s == -1) return;
+  if (it.s >= 0) {
     s = it.s;
     qt = it.t;
     kvh = (int)(blockIdx.x % P.Hkv);

@@ -263,22 +263,23 @@ def test_prefill_large_grid_negative_scale(dev, mb):
 
 
 @pytest.mark.parametrize("mb", WIDE)
-def test_prefill_many_sequences_round_order(dev, mb):
-    """More than 64 sequences (the launch order by query-tile rounds), every token."""
+@pytest.mark.parametrize("S", [80, 300])
+def test_prefill_many_sequences(dev, mb, S):
+    """80 sequences (ranked launch order, two sequences per lane of the rank
+    search) and 300 (more than 256: the order by query-tile rounds), every token."""
     rng = np.random.default_rng(63)
-    S = 80
     x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=63, context_lens=rng.integers(0, 400, size=S),
                               query_lens=rng.integers(1, 60, size=S), max_blocks_per_seq=mb)
     say(f"prefill {S} sequences: {x.num_query_tokens} tokens")
     check_all(x, run(x, dev), f"{S} sequences")
 
 
-@pytest.mark.parametrize("S", [5, 70])
+@pytest.mark.parametrize("S", [5, 70, 260])
 def test_prefill_tokens_past_max_query_len_not_computed(dev, S):
     """max_query_len = 64 below the longest chunk: chunk tokens 0..63 of every
     sequence are right, the later ones keep what the output held (64 is a whole
     number of query tiles in every launch shape at G = 8). Both launch orders
-    (by cost up to 64 sequences, by rounds above)."""
+    (by cost up to 256 sequences, by rounds above)."""
     rng = np.random.default_rng(64 + S)
     ql = rng.integers(1, 200, size=S)
     ql[0] = 199
@@ -299,10 +300,11 @@ def test_prefill_tokens_past_max_query_len_not_computed(dev, S):
 
 
 @pytest.mark.parametrize("mb", WIDE)
-def test_prefill_64_sequences_ranked_order(dev, mb):
-    """64 sequences, the most that take the launch order ranked by cost, every token."""
+@pytest.mark.parametrize("S", [64, 256])
+def test_prefill_ranked_order_slot_edges(dev, mb, S):
+    """64 sequences (one per lane of the rank search) and 256 (four per lane,
+    the most that take the launch order ranked by cost), every token."""
     rng = np.random.default_rng(66)
-    S = 64
     x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=66, context_lens=rng.integers(0, 500, size=S),
                               query_lens=rng.integers(1, 100, size=S), max_blocks_per_seq=mb)
     say(f"prefill {S} sequences (ranked order): {x.num_query_tokens} tokens")
@@ -332,3 +334,18 @@ def test_prefill_mixed_batch_with_chunks_longer_than_their_sequence(dev):
     say(f"prefill mixed batch, chunks longer than their sequence: {x.num_query_tokens} tokens")
     got = check_all(x, run(x, dev), "negative positions, mixed batch")
     assert (got[0:100] == 0).all() and (got[qsl[2]:qsl[2] + 40] == 0).all()
+
+
+@pytest.mark.parametrize("S", [16, 64, 100])
+def test_prefill_fresh_prompts_of_different_lengths(dev, S):
+    """No prefix, chunks of different lengths (every sequence's prefix is the
+    same: up to 64 sequences the ranked search, above it the round order), and
+    the same with equal chunks (the equal-sequence shortcut), every token."""
+    rng = np.random.default_rng(70 + S)
+    for label, ql in (("mixed chunks", rng.integers(1, 200, size=S)), ("equal chunks", np.full(S, 77))):
+        x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=70 + S, context_lens=[0] * S, query_lens=ql)
+        say(f"prefill {S} fresh prompts, {label}: {x.num_query_tokens} tokens")
+        check_all(x, run(x, dev), f"{S} fresh prompts, {label}")
+        # the same prefix for every sequence, not zero
+        x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=71 + S, context_lens=[300] * S, query_lens=ql)
+        check_all(x, run(x, dev), f"{S} prompts behind equal prefixes, {label}")
