@@ -151,8 +151,33 @@ struct WorkItem {
   int s, t;  // s = -1: no item; s = -2: every sequence has the same prefix (take the round order)
 };
 
+// A sequence's extents, clamped so that no data value can send a read out of
+// bounds: chunk tokens [qb, qb + Q) of q and out, L keys in its block table.
+struct SeqExtent {
+  int qb, Q, L;
+};
+
+__device__ __forceinline__ SeqExtent load_extent(const PrefillParams& P, int s) {
+  const int qb_raw = P.qsl[s], qe_raw = P.qsl[s + 1], L_raw = P.sl[s];
+  const int qb = min(max(qb_raw, 0), P.T);
+  const int qe = min(max(qe_raw, qb), P.T);
+  return {qb, qe - qb, min(max(L_raw, 0), P.MB * kBS)};
+}
+
+// The extents of sequence s (wave-uniform) from the lane that holds it.
 template <int SLOTS>
-__device__ WorkItem item_by_cost(const PrefillParams& P, int g, int nq, int lane) {
+__device__ __forceinline__ SeqExtent slot_extent(const SeqExtent (&e)[SLOTS], int s) {
+  SeqExtent r{0, 0, 0};
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k)
+    if (k == (s >> 6))
+      r = {__builtin_amdgcn_readlane(e[k].qb, s & 63), __builtin_amdgcn_readlane(e[k].Q, s & 63),
+           __builtin_amdgcn_readlane(e[k].L, s & 63)};
+  return r;
+}
+
+template <int SLOTS>
+__device__ WorkItem item_by_cost(const PrefillParams& P, const SeqExtent (&e)[SLOTS], int g, int nq, int lane) {
   const int slots = SLOTS == 1 ? 1 : (P.S + 63) / 64;  // 1 .. SLOTS, wave-uniform
   const uint32_t QT = (uint32_t)P.QT;
   uint32_t base[SLOTS], Q[SLOTS], last[SLOTS];
@@ -161,15 +186,9 @@ __device__ WorkItem item_by_cost(const PrefillParams& P, int g, int nq, int lane
   for (int k = 0; k < SLOTS; ++k) {
     base[k] = Q[k] = 0u;
     n[k] = 0;
-    const int sq = 64 * k + lane;
-    if (k < slots && sq < P.S) {
-      int qb = P.qsl[sq], qe = P.qsl[sq + 1];
-      qb = min(max(qb, 0), P.T);
-      qe = min(max(qe, qb), P.T);
-      const int L = min(max(P.sl[sq], 0), P.MB * kBS);
-      const uint32_t Qall = (uint32_t)(qe - qb);
-      base[k] = (uint32_t)L + ((uint32_t)P.T - Qall);  // key of the chunk's position 0, shifted by T
-      Q[k] = min(Qall, (uint32_t)nq * QT);             // tiles past the grid's nq are not computed
+    if (k < slots && 64 * k + lane < P.S) {
+      base[k] = (uint32_t)e[k].L + ((uint32_t)P.T - (uint32_t)e[k].Q);  // key of the chunk's position 0, shifted by T
+      Q[k] = min((uint32_t)e[k].Q, (uint32_t)nq * QT);                  // tiles past the grid's nq are not computed
       n[k] = (int)((Q[k] + QT - 1) / QT);
     }
     last[k] = base[k] + Q[k];  // the key of the sequence's last tile
@@ -254,6 +273,44 @@ __device__ WorkItem item_by_cost(const PrefillParams& P, int g, int nq, int lane
   return {-1, 0};  // unreachable: F counts exactly the items above
 }
 
+// Workgroup blockIdx.x's item: sequence, KV head, query tile and the
+// sequence's extents (s = -1: none).
+struct Item {
+  int s, kvh, qt;
+  SeqExtent e;
+};
+
+// Round r = b / pairs takes query tile nq - 1 - r of every (sequence, KV
+// head) pair, the pairs rotated by r.
+__device__ __forceinline__ Item round_order_item(const PrefillParams& P, int nq) {
+  const int pairs = P.S * P.Hkv;
+  const int r = (int)(blockIdx.x / pairs);
+  const int pair = ((int)(blockIdx.x % pairs) + r) % pairs;
+  return {pair / P.Hkv, pair % P.Hkv, nq - 1 - r, {0, 0, 0}};
+}
+
+// The ranked item (or the round order where item_by_cost defers to it), with
+// the extents read from the lanes that loaded them for the search: no
+// second round trip to memory.
+template <int SLOTS>
+__device__ __forceinline__ Item find_item(const PrefillParams& P, int nq, int lane) {
+  // Every slot loads (sequence index clamped into the batch, S >= 1) and the
+  // lanes past the batch drop theirs afterwards: the loads of all slots go
+  // out together, where a load under a per-slot branch would wait for its
+  // own round trip.
+  SeqExtent e[SLOTS];
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k) e[k] = load_extent(P, min(64 * k + lane, P.S - 1));
+#pragma unroll
+  for (int k = 0; k < SLOTS; ++k)
+    if (64 * k + lane >= P.S) e[k] = {0, 0, 0};
+  const WorkItem w = item_by_cost<SLOTS>(P, e, (int)(blockIdx.x / P.Hkv), nq, lane);
+  if (w.s == -1) return {-1, 0, 0, {0, 0, 0}};
+  Item it = w.s >= 0 ? Item{w.s, (int)(blockIdx.x % P.Hkv), w.t, {0, 0, 0}} : round_order_item(P, nq);
+  it.e = slot_extent(e, it.s);
+  return it;
+}
+
 template <typename T, int D, int NW, int NTW, int TB, int SHD, int KS>
 __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
   typedef typename H16<T>::x8 tx8;
@@ -287,32 +344,15 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
   // see the most keys; with equal prefixes that is the order by cost), the
   // pairs rotated by r: workgroups go to the XCDs round-robin, and without the
   // rotation each XCD would take the same few pairs in every round.
-  const int pairs = P.S * P.Hkv;
-  const int nq = (int)(gridDim.x / pairs);
-  int s, kvh, qt;
-  const int rank = (int)(blockIdx.x / P.Hkv);
-  const WorkItem it = P.S <= 64            ? item_by_cost<1>(P, rank, nq, lane)
-                      : P.S <= kRankedSeqs ? item_by_cost<4>(P, rank, nq, lane)
-                                           : WorkItem{-2, 0};
-  if (it.s == -1) return;
-  if (it.s >= 0) {
-    s = it.s;
-    qt = it.t;
-    kvh = (int)(blockIdx.x % P.Hkv);
-  } else {
-    const int r = (int)(blockIdx.x / pairs);
-    const int pair = ((int)(blockIdx.x % pairs) + r) % pairs;
-    qt = nq - 1 - r;
-    s = pair / P.Hkv;
-    kvh = pair % P.Hkv;
-  }
-  // Extents, clamped so that no data value can send a read out of bounds.
-  int qb = P.qsl[s], qe = P.qsl[s + 1];
-  qb = min(max(qb, 0), P.T);
-  qe = min(max(qe, qb), P.T);
-  const int Q = qe - qb;
-  int L = P.sl[s];
-  L = min(max(L, 0), P.MB * kBS);
+  const int nq = (int)(gridDim.x / (P.S * P.Hkv));
+  const Item it = P.S <= 64 ? find_item<1>(P, nq, lane) : P.S <= kRankedSeqs ? find_item<4>(P, nq, lane) : [&] {
+    Item r = round_order_item(P, nq);
+    r.e = load_extent(P, r.s);
+    return r;
+  }();
+  if (it.s < 0) return;
+  const int s = it.s, kvh = it.kvh, qt = it.qt;
+  const int qb = it.e.qb, Q = it.e.Q, L = it.e.L;
   const int i0 = qt * P.QT;
   if (i0 >= Q) return;
   const int i1 = min(i0 + P.QT, Q);
