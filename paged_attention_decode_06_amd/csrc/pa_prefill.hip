@@ -396,9 +396,13 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
   // B operands of the QK MFMA: lane holds q[row][kk*32 + 8*grp .. +8].
   // A negative scale is folded into q (an exact sign flip), so that the
   // softmax below scales by |scale| and takes its running max on the raw
-  // scores (the max commutes with a non-negative scale).
-  const bool neg_scale = P.scale2 < 0.f;
-  const float s2 = fabsf(P.scale2);
+  // scores (the max commutes with a non-negative scale). A zero scale is
+  // folded in as q = 0 with scale 1: every score is then exactly 0, and
+  // every visible key weighs exactly 1, as with the zero scale itself; the
+  // softmax thus always scales by a positive number, which sends masked
+  // scores (-inf) to exactly 0.
+  const bool neg_scale = P.scale2 < 0.f, zero_scale = P.scale2 == 0.f;
+  const float s2 = zero_scale ? 1.f : fabsf(P.scale2);
   tx8 qv[NTW][KK];
 #pragma unroll
   for (int jj = 0; jj < NTW; ++jj) {
@@ -410,6 +414,7 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
       u32x4 x = {0u, 0u, 0u, 0u};
       if (valid[jj]) x = ld16(qrow + kk * 32 + grp * 8);
       if (neg_scale) x ^= (u32x4){0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+      if (zero_scale) x = (u32x4){0u, 0u, 0u, 0u};
       qv[jj][kk] = __builtin_bit_cast(tx8, x);
     }
   }
@@ -442,65 +447,13 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) ones4[i] = (T)1.0f;
 
-  // The math of tile t in three steps: the QK scores of N-tile jj from K
-  // operands ka; the online-softmax update of that N-tile (running max,
-  // exp-sum, rescale of its accumulators), which hands back P rounded to the
-  // 16-bit type; and P.V (below, per tile shape).
+  // The QK scores of N-tile jj from K operands ka.
   auto qk_scores = [&](const tx8 (&ka)[TB][KK], int jj, f32x4 (&sc)[TB]) {
 #pragma unroll
     for (int b = 0; b < TB; ++b) {
       sc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int kk = 0; kk < KK; ++kk) sc[b] = H16<T>::mma32(ka[b][kk], qv[jj][kk], sc[b]);
-    }
-  };
-  auto softmax_step = [&](const f32x4 (&sc)[TB], int jj, int t, T (&pb)[TB][4]) {
-    const int tok0 = t * TB * kBS;
-    const bool full = tok0 + TB * kBS - 1 <= wave_min_pos;  // no row of the wave needs the mask here
-    float mx = -INFINITY;
-    if (full) {
-#pragma unroll
-      for (int b = 0; b < TB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[b][i]);
-      mx = rows_max(mx);
-      const float mnew = fmaxf(m[jj], mx * s2);  // finite: key 0 is in every row's first tile
-      const float alpha = fast_exp2(m[jj] - mnew);
-      m[jj] = mnew;
-#pragma unroll
-      for (int b = 0; b < TB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pb[b][i] = (T)fast_exp2(__builtin_fmaf(sc[b][i], s2, -mnew));
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-        for (int a = 0; a < NACC; ++a) acc[jj][a] *= alpha;
-        accl[jj] *= alpha;
-      }
-    } else {
-      bool ok[TB][4];
-#pragma unroll
-      for (int b = 0; b < TB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ok[b][i] = tok0 + b * kBS + 4 * grp + i <= posc[jj];
-          mx = fmaxf(mx, ok[b][i] ? sc[b][i] : -INFINITY);
-        }
-      mx = rows_max(mx);
-      // A row with no visible key here keeps its max (fmaxf drops the NaN of
-      // -inf * 0); with a key split, a key group's first tile can hide every
-      // key from a row, and then the max stays -inf and alpha must be 1.
-      const float mnew = fmaxf(m[jj], mx * s2);
-      const float alpha = m[jj] == mnew ? 1.f : fast_exp2(m[jj] - mnew);
-      m[jj] = mnew;
-#pragma unroll
-      for (int b = 0; b < TB; ++b)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) pb[b][i] = (T)(ok[b][i] ? fast_exp2(__builtin_fmaf(sc[b][i], s2, -mnew)) : 0.f);
-      if (__builtin_amdgcn_ballot_w64(alpha != 1.f)) {
-#pragma unroll
-        for (int a = 0; a < NACC; ++a) acc[jj][a] *= alpha;
-        accl[jj] *= alpha;
-      }
     }
   };
   auto pack_p2 = [&](const T (&p0)[4], const T (&p1)[4]) {  // two blocks of P as one B operand, keys 4grp+i, 16+4grp+i
@@ -623,22 +576,6 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
 #pragma unroll
       for (int jj = 0; jj < NTW; ++jj) qk_scores(ka, jj, sc[jj]);
     };
-    // Softmax of key tile u from its scores: P of each N-tile as the B
-    // operand of the P.V products (the accumulators are rescaled here).
-    auto softmax_pack = [&](int u, const f32x4 (&sc)[NTW][TB], PV (&pv)[NTW]) {
-#pragma unroll
-      for (int jj = 0; jj < NTW; ++jj) {
-        T pb[TB][4];
-        softmax_step(sc[jj], jj, u, pb);
-        if constexpr (TB == 1) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pv[jj].p[0][i] = pb[0][i];
-        } else {
-#pragma unroll
-          for (int pp = 0; pp < NPB; ++pp) pv[jj].p[pp] = pack_p2(pb[2 * pp], pb[2 * pp + 1]);
-        }
-      }
-    };
     // P.V products (and row sums) from the V tile at vt. V^T operand of
     // M-tile mt (head dims 16mt .. 16mt+15) for the pair of blocks 2pp,
     // 2pp + 1: keys 4grp .. 4grp+3 of each, in the order the QK accumulator
@@ -672,6 +609,121 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
         }
       }
     };
+    // The math of key tile t: QK scores, online-softmax update (running max,
+    // rescale of the accumulators), P rounded to the 16-bit type, P.V. The
+    // code runs straight through but for two branches: the causal mask, only
+    // on tiles that reach past the wave's smallest position (masked scores
+    // become -inf), and the rescale, skipped when no row's max grew (rare once
+    // the maxima settle). P and the P.V products of both N-tiles are then one
+    // basic block, in which the exponentials of one N-tile issue while the
+    // matrix cores run the products of the other.
+    auto tile_math = [&](const u32x4* kt, const u32x4* vt, int t) __attribute__((always_inline)) {
+      f32x4 sc[NTW][TB];
+      qk_tile(kt, sc);
+      const int tok0 = t * TB * kBS;
+      if (tok0 + TB * kBS - 1 > wave_min_pos) {
+#pragma unroll
+        for (int jj = 0; jj < NTW; ++jj)
+#pragma unroll
+          for (int b = 0; b < TB; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+              if (tok0 + b * kBS + 4 * grp + i > posc[jj]) sc[jj][b][i] = -INFINITY;
+      }
+      float mb[NTW], alpha[NTW];
+      bool grew = false;
+#pragma unroll
+      for (int jj = 0; jj < NTW; ++jj) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[jj][b][i]);
+        mx = rows_max(mx);
+        // A row with no visible key so far keeps max -inf (with a key split,
+        // a key group's first tile can hide every key from a row): alpha is
+        // then 1, and P is taken against 0 (every score of the row is -inf).
+        const float mnew = fmaxf(m[jj], mx * s2);
+        alpha[jj] = m[jj] == mnew ? 1.f : fast_exp2(m[jj] - mnew);
+        grew |= alpha[jj] != 1.f;
+        m[jj] = mnew;
+        mb[jj] = mnew == -INFINITY ? 0.f : mnew;
+      }
+      if (__builtin_amdgcn_ballot_w64(grew)) {
+#pragma unroll
+        for (int jj = 0; jj < NTW; ++jj) {
+#pragma unroll
+          for (int a = 0; a < NACC; ++a) acc[jj][a] *= alpha[jj];
+          accl[jj] *= alpha[jj];
+        }
+      }
+      PV pv[NTW];
+      auto make_p = [&](int jj) __attribute__((always_inline)) {  // P of N-tile jj, as P.V operands
+        T pb[TB][4];
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pb[b][i] = (T)fast_exp2(__builtin_fmaf(sc[jj][b][i], s2, -mb[jj]));
+        if constexpr (TB == 1) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) pv[jj].p[0][i] = pb[0][i];
+        } else {
+#pragma unroll
+          for (int pp = 0; pp < NPB; ++pp) pv[jj].p[pp] = pack_p2(pb[2 * pp], pb[2 * pp + 1]);
+        }
+      };
+      if constexpr (NTW == 2 && TB == 4) {
+        // Two N-tiles and two block pairs: four phases, fenced for the
+        // scheduler (sched_barrier) so that no phase's instructions move into
+        // another, with the issue order inside two of them set by
+        // sched_group_barrier (masks: 0x8 MFMA, 0x100 LDS read, 0x402 vector
+        // ALU and transcendental). (1) V reads of pair 0 beside P of N-tile 0;
+        // (2) P.V of N-tile 0, pair 0, one MFMA then five vector instructions
+        // of P of N-tile 1 at a time; (3) P.V of N-tile 1, pair 0, one MFMA
+        // then two V reads of pair 1 at a time; (4) P.V of pair 1.
+        const char* vb = reinterpret_cast<const char*>(vt);
+        auto read_v = [&](int pp, tx8 (&vo)[NACC]) __attribute__((always_inline)) {
+#pragma unroll
+          for (int mt = 0; mt < NACC; ++mt) {
+            const i16x4 lo = lds_read_tr16(vb + vlo[mt] + 2 * pp * 16 * KCH * 16);
+            const i16x4 hi = lds_read_tr16(vb + vlo[mt] + (2 * pp + 1) * 16 * KCH * 16);
+            vo[mt] = __builtin_bit_cast(tx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          }
+        };
+        auto mma_pv = [&](const tx8 (&vo)[NACC], int jj, int pp) __attribute__((always_inline)) {
+#pragma unroll
+          for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma32(vo[mt], pv[jj].p[pp], acc[jj][mt]);
+          accl[jj] = H16<T>::mma32(ones8, pv[jj].p[pp], accl[jj]);
+        };
+        tx8 vo0[NACC], vo1[NACC];
+        read_v(0, vo0);
+        make_p(0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_pv(vo0, 0, 0);
+        make_p(1);
+#pragma unroll
+        for (int i = 0; i < NACC + 1; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mma_pv(vo0, 1, 0);
+        read_v(1, vo1);
+#pragma unroll
+        for (int i = 0; i < NACC; ++i) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mma_pv(vo1, 0, 1);
+        mma_pv(vo1, 1, 1);
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < NTW; ++jj) make_p(jj);
+        pv_apply(vt, pv);
+      }
+    };
     // Iteration σ (slot σ % NSL) starts the loads of step σ + SHD, runs this
     // wave's tile of the step (QK products, softmax, P.V products), waits
     // for the loads of step σ + 1 and ends with one barrier. The loop runs
@@ -694,13 +746,7 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
         const int t = step * KS + kg;
         auto load = [&](u32x4* kn, u32x4* vn) { fetch(step + SHD, kn, vn); };
         auto math = [&](const u32x4* kc, const u32x4* vc) {
-          if (t < ntiles) {
-            f32x4 sc[NTW][TB];
-            PV pv[NTW];
-            qk_tile(kc, sc);
-            softmax_pack(t, sc, pv);
-            pv_apply(vc, pv);
-          }
+          if (t < ntiles) tile_math(kc, vc, t);
         };
         constexpr int nx = (d + SHD) % NSL;
         with_slots(kst + nx * KS * TCH, vst + nx * KS * TCH, kst + (d * KS + kg) * TCH, vst + (d * KS + kg) * TCH,
