@@ -672,15 +672,15 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
           for (int pp = 0; pp < NPB; ++pp) pv[jj].p[pp] = pack_p2(pb[2 * pp], pb[2 * pp + 1]);
         }
       };
-      if constexpr (NTW == 2 && TB == 4) {
-        // Two N-tiles and two block pairs: four phases, fenced for the
-        // scheduler (sched_barrier) so that no phase's instructions move into
-        // another, with the issue order inside two of them set by
-        // sched_group_barrier (masks: 0x8 MFMA, 0x100 LDS read, 0x402 vector
-        // ALU and transcendental). (1) V reads of pair 0 beside P of N-tile 0;
-        // (2) P.V of N-tile 0, pair 0, one MFMA then five vector instructions
-        // of P of N-tile 1 at a time; (3) P.V of N-tile 1, pair 0, one MFMA
-        // then two V reads of pair 1 at a time; (4) P.V of pair 1.
+      if constexpr (TB == 4 && (NTW == 1 || NTW == 2)) {
+        // Block pairs 0 and 1 in scheduler-fenced phases (sched_barrier), with
+        // the issue order inside some set by sched_group_barrier (masks: 0x8
+        // MFMA, 0x100 LDS read, 0x402 vector ALU and transcendental): (1) V
+        // reads of pair 0 beside P of N-tile 0; with two N-tiles, (2) P.V of
+        // N-tile 0, pair 0, one MFMA then five vector instructions of P of
+        // N-tile 1 at a time; (3) P.V of the last N-tile, pair 0, one MFMA then
+        // two V reads of pair 1 at a time; (4) P.V of pair 1. Left to itself
+        // the compiler reads V just before each product and waits on it.
         const char* vb = reinterpret_cast<const char*>(vt);
         auto read_v = [&](int pp, tx8 (&vo)[NACC]) __attribute__((always_inline)) {
 #pragma unroll
@@ -699,15 +699,17 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
         read_v(0, vo0);
         make_p(0);
         __builtin_amdgcn_sched_barrier(0);
-        mma_pv(vo0, 0, 0);
-        make_p(1);
+        if constexpr (NTW == 2) {
+          mma_pv(vo0, 0, 0);
+          make_p(1);
 #pragma unroll
-        for (int i = 0; i < NACC + 1; ++i) {
-          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+          for (int i = 0; i < NACC + 1; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        mma_pv(vo0, 1, 0);
+        mma_pv(vo0, NTW - 1, 0);
         read_v(1, vo1);
 #pragma unroll
         for (int i = 0; i < NACC; ++i) {
@@ -716,8 +718,8 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
         }
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_barrier(0);
-        mma_pv(vo1, 0, 1);
-        mma_pv(vo1, 1, 1);
+#pragma unroll
+        for (int jj = 0; jj < NTW; ++jj) mma_pv(vo1, jj, 1);
       } else {
 #pragma unroll
         for (int jj = 0; jj < NTW; ++jj) make_p(jj);
