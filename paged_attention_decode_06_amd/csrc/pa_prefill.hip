@@ -568,13 +568,51 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
       vlo[mt] = (R * KCH + 2 * (mt ^ (R & 7)) + ((g >> 1) & 1)) * 16 + (g & 1) * 8;
     }
     auto qk_tile = [&](const u32x4* kt, f32x4 (&sc)[NTW][TB]) {  // QK scores of the K tile at kt
-      tx8 ka[TB][KK];
+      if constexpr (NTW == 1 && KK == 8) {
+        // head_dim 256: a tile's K operands would take 128 registers, so they
+        // are read one block ahead (two blocks of 32 registers in turn), the
+        // reads of block b + 1 interleaved with the products of block b
+        // (sched_group_barrier: one MFMA, one LDS read). Left to itself the
+        // compiler read each operand just before its product and waited on it.
+        tx8 k0[KK], k1[KK];
+        auto read_k = [&](int b, tx8 (&ka)[KK]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int b = 0; b < TB; ++b)
+          for (int kk = 0; kk < KK; ++kk) ka[kk] = __builtin_bit_cast(tx8, kt[klo[kk] + b * 16 * KCH]);
+        };
+        auto mma_k = [&](int b, const tx8 (&ka)[KK]) __attribute__((always_inline)) {
+          sc[0][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) ka[b][kk] = __builtin_bit_cast(tx8, kt[klo[kk] + b * 16 * KCH]);
+          for (int kk = 0; kk < KK; ++kk) sc[0][b] = H16<T>::mma32(ka[kk], qv[0][kk], sc[0][b]);
+        };
+        read_k(0, k0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int jj = 0; jj < NTW; ++jj) qk_scores(ka, jj, sc[jj]);
+        for (int b = 0; b < TB; ++b) {
+          if (b % 2 == 0) {
+            mma_k(b, k0);
+            if (b + 1 < TB) read_k(b + 1, k1);
+          } else {
+            mma_k(b, k1);
+            if (b + 1 < TB) read_k(b + 1, k0);
+          }
+          if (b + 1 < TB) {
+#pragma unroll
+            for (int i = 0; i < KK; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+        tx8 ka[TB][KK];
+#pragma unroll
+        for (int b = 0; b < TB; ++b)
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) ka[b][kk] = __builtin_bit_cast(tx8, kt[klo[kk] + b * 16 * KCH]);
+#pragma unroll
+        for (int jj = 0; jj < NTW; ++jj) qk_scores(ka, jj, sc[jj]);
+      }
     };
     // P.V products (and row sums) from the V tile at vt. V^T operand of
     // M-tile mt (head dims 16mt .. 16mt+15) for the pair of blocks 2pp,
