@@ -314,7 +314,6 @@ __device__ __forceinline__ Item find_item(const PrefillParams& P, int nq, int la
 template <typename T, int D, int NW, int NTW, int TB, int SHD, int KS>
 __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
   typedef typename H16<T>::x8 tx8;
-  typedef typename H16<T>::x4 tx4;
   extern __shared__ float smem[];
   constexpr int KK = D / 32;    // QK MFMAs per block and N-tile
   constexpr int NACC = D / 16;  // output tiles (16 head dims each) per N-tile
@@ -443,9 +442,6 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
   tx8 ones8;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones8[i] = (T)1.0f;
-  tx4 ones4;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) ones4[i] = (T)1.0f;
 
   // The QK scores of N-tile jj from K operands ka.
   auto qk_scores = [&](const tx8 (&ka)[TB][KK], int jj, f32x4 (&sc)[TB]) {
@@ -478,16 +474,14 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
     // chunk c at c ^ 2 (r % 8) (the transpose read takes chunk pairs 2mt,
     // 2mt+1 from rows 4grp .. 4grp+3, and eight consecutive rows then hit
     // eight distinct 32-byte bank groups). Each lane loads the global chunk
-    // that its LDS position holds. A tile is TB blocks of 16 keys; the P.V
-    // products take them in pairs (16x16x32 MFMAs), or one block at a time
-    // with TB = 1 (16x16x16 MFMAs, half the work in the same issue time).
+    // that its LDS position holds. A tile is four blocks of 16 keys; the P.V
+    // products take them in two pairs (16x16x32 MFMAs).
     static_assert(KCH == 16 || KCH == 32, "head_dim 128 or 256");
     constexpr int TCH = TB * 16 * KCH;               // chunks per K (or V) tile
     constexpr int RPW = 64 / KCH;                    // tile rows one load of a wave covers
-    static_assert(TB == 1 || TB % 2 == 0, "one block, or pairs of blocks");
-    constexpr int NPB = TB == 1 ? 1 : TB / 2;        // P.V products per output tile and step
+    static_assert(TB == 4 && ((D == 128 && NTW == 2) || (D == 256 && NTW == 1)), "the launch shapes' tiles");
     struct PV {                                       // P as the B operands of the P.V products
-      std::conditional_t<TB == 1, tx4, tx8> p[NPB];
+      tx8 p[2];                                       // block pairs 0 and 1
     };
     // LDS: NSL slots (step % NSL) of KS tiles each, K [NSL][KS][TB*16][KCH]
     // then V [NSL][KS][TB*16][KCH]. A step is KS consecutive key tiles, one
@@ -568,7 +562,7 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
       vlo[mt] = (R * KCH + 2 * (mt ^ (R & 7)) + ((g >> 1) & 1)) * 16 + (g & 1) * 8;
     }
     auto qk_tile = [&](const u32x4* kt, f32x4 (&sc)[NTW][TB]) {  // QK scores of the K tile at kt
-      if constexpr (NTW == 1 && KK == 8) {
+      if constexpr (D == 256) {
         // head_dim 256: a tile's K operands would take 128 registers, so they
         // are read one block ahead (two blocks of 32 registers in turn), the
         // reads of block b + 1 interleaved with the products of block b
@@ -614,38 +608,22 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
         for (int jj = 0; jj < NTW; ++jj) qk_scores(ka, jj, sc[jj]);
       }
     };
-    // P.V products (and row sums) from the V tile at vt. V^T operand of
-    // M-tile mt (head dims 16mt .. 16mt+15) for the pair of blocks 2pp,
-    // 2pp + 1: keys 4grp .. 4grp+3 of each, in the order the QK accumulator
-    // hands P over (with TB = 1, those of block 0 alone).
-    auto pv_apply = [&](const u32x4* vt, const PV (&pv)[NTW]) {
-      const char* vb = reinterpret_cast<const char*>(vt);
+    // P.V products (and row sums). V^T operand of M-tile mt (head dims
+    // 16mt .. 16mt+15) for block pair pp (blocks 2pp, 2pp + 1 of the V tile at
+    // vb): keys 4grp .. 4grp+3 of each, in the order the QK accumulator hands
+    // P over.
+    auto read_v = [&](const char* vb, int pp, tx8 (&vo)[NACC]) __attribute__((always_inline)) {
 #pragma unroll
-      for (int pp = 0; pp < NPB; ++pp) {
-        std::conditional_t<TB == 1, tx4, tx8> vo[NACC];
-#pragma unroll
-        for (int mt = 0; mt < NACC; ++mt) {
-          const i16x4 lo = lds_read_tr16(vb + vlo[mt] + 2 * pp * 16 * KCH * 16);
-          if constexpr (TB == 1) {
-            vo[mt] = __builtin_bit_cast(tx4, lo);
-          } else {
-            const i16x4 hi = lds_read_tr16(vb + vlo[mt] + (2 * pp + 1) * 16 * KCH * 16);
-            vo[mt] = __builtin_bit_cast(tx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
-        }
-#pragma unroll
-        for (int jj = 0; jj < NTW; ++jj) {
-          if constexpr (TB == 1) {
-#pragma unroll
-            for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma16(vo[mt], pv[jj].p[0], acc[jj][mt]);
-            accl[jj] = H16<T>::mma16(ones4, pv[jj].p[0], accl[jj]);
-          } else {
-#pragma unroll
-            for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma32(vo[mt], pv[jj].p[pp], acc[jj][mt]);
-            accl[jj] = H16<T>::mma32(ones8, pv[jj].p[pp], accl[jj]);
-          }
-        }
+      for (int mt = 0; mt < NACC; ++mt) {
+        const i16x4 lo = lds_read_tr16(vb + vlo[mt] + 2 * pp * 16 * KCH * 16);
+        const i16x4 hi = lds_read_tr16(vb + vlo[mt] + (2 * pp + 1) * 16 * KCH * 16);
+        vo[mt] = __builtin_bit_cast(tx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
       }
+    };
+    auto mma_pv = [&](const tx8 (&vo)[NACC], const PV& pv, int jj, int pp) __attribute__((always_inline)) {
+#pragma unroll
+      for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma32(vo[mt], pv.p[pp], acc[jj][mt]);
+      accl[jj] = H16<T>::mma32(ones8, pv.p[pp], accl[jj]);
     };
     // The math of key tile t: QK scores, online-softmax update (running max,
     // rescale of the accumulators), P rounded to the 16-bit type, P.V. The
@@ -702,67 +680,43 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
         for (int b = 0; b < TB; ++b)
 #pragma unroll
           for (int i = 0; i < 4; ++i) pb[b][i] = (T)fast_exp2(__builtin_fmaf(sc[jj][b][i], s2, -mb[jj]));
-        if constexpr (TB == 1) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) pv[jj].p[0][i] = pb[0][i];
-        } else {
-#pragma unroll
-          for (int pp = 0; pp < NPB; ++pp) pv[jj].p[pp] = pack_p2(pb[2 * pp], pb[2 * pp + 1]);
-        }
+        pv[jj].p[0] = pack_p2(pb[0], pb[1]);
+        pv[jj].p[1] = pack_p2(pb[2], pb[3]);
       };
-      if constexpr (TB == 4 && (NTW == 1 || NTW == 2)) {
-        // Block pairs 0 and 1 in scheduler-fenced phases (sched_barrier), with
-        // the issue order inside some set by sched_group_barrier (masks: 0x8
-        // MFMA, 0x100 LDS read, 0x402 vector ALU and transcendental): (1) V
-        // reads of pair 0 beside P of N-tile 0; with two N-tiles, (2) P.V of
-        // N-tile 0, pair 0, one MFMA then five vector instructions of P of
-        // N-tile 1 at a time; (3) P.V of the last N-tile, pair 0, one MFMA then
-        // two V reads of pair 1 at a time; (4) P.V of pair 1. Left to itself
-        // the compiler reads V just before each product and waits on it.
-        const char* vb = reinterpret_cast<const char*>(vt);
-        auto read_v = [&](int pp, tx8 (&vo)[NACC]) __attribute__((always_inline)) {
+      // Block pairs 0 and 1 in scheduler-fenced phases (sched_barrier), with
+      // the issue order inside some set by sched_group_barrier (masks: 0x8
+      // MFMA, 0x100 LDS read, 0x402 vector ALU and transcendental): (1) V
+      // reads of pair 0 beside P of N-tile 0; with two N-tiles, (2) P.V of
+      // N-tile 0, pair 0, one MFMA then five vector instructions of P of
+      // N-tile 1 at a time; (3) P.V of the last N-tile, pair 0, one MFMA then
+      // two V reads of pair 1 at a time; (4) P.V of pair 1. Left to itself
+      // the compiler reads V just before each product and waits on it.
+      const char* vb = reinterpret_cast<const char*>(vt);
+      tx8 vo0[NACC], vo1[NACC];
+      read_v(vb, 0, vo0);
+      make_p(0);
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (NTW == 2) {
+        mma_pv(vo0, pv[0], 0, 0);
+        make_p(1);
 #pragma unroll
-          for (int mt = 0; mt < NACC; ++mt) {
-            const i16x4 lo = lds_read_tr16(vb + vlo[mt] + 2 * pp * 16 * KCH * 16);
-            const i16x4 hi = lds_read_tr16(vb + vlo[mt] + (2 * pp + 1) * 16 * KCH * 16);
-            vo[mt] = __builtin_bit_cast(tx8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          }
-        };
-        auto mma_pv = [&](const tx8 (&vo)[NACC], int jj, int pp) __attribute__((always_inline)) {
-#pragma unroll
-          for (int mt = 0; mt < NACC; ++mt) acc[jj][mt] = H16<T>::mma32(vo[mt], pv[jj].p[pp], acc[jj][mt]);
-          accl[jj] = H16<T>::mma32(ones8, pv[jj].p[pp], accl[jj]);
-        };
-        tx8 vo0[NACC], vo1[NACC];
-        read_v(0, vo0);
-        make_p(0);
-        __builtin_amdgcn_sched_barrier(0);
-        if constexpr (NTW == 2) {
-          mma_pv(vo0, 0, 0);
-          make_p(1);
-#pragma unroll
-          for (int i = 0; i < NACC + 1; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        mma_pv(vo0, NTW - 1, 0);
-        read_v(1, vo1);
-#pragma unroll
-        for (int i = 0; i < NACC; ++i) {
+        for (int i = 0; i < NACC + 1; ++i) {
           __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(0x402, 5, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
         __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int jj = 0; jj < NTW; ++jj) mma_pv(vo1, jj, 1);
-      } else {
-#pragma unroll
-        for (int jj = 0; jj < NTW; ++jj) make_p(jj);
-        pv_apply(vt, pv);
       }
+      mma_pv(vo0, pv[NTW - 1], NTW - 1, 0);
+      read_v(vb, 1, vo1);
+#pragma unroll
+      for (int i = 0; i < NACC; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int jj = 0; jj < NTW; ++jj) mma_pv(vo1, pv[jj], jj, 1);
     };
     // Iteration σ (slot σ % NSL) starts the loads of step σ + SHD, runs this
     // wave's tile of the step (QK products, softmax, P.V products), waits
