@@ -492,8 +492,8 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
     constexpr int NSL = SHD + 1;
     u32x4* kst = reinterpret_cast<u32x4*>(smem);
     u32x4* vst = kst + NSL * KS * TCH;
-    // Loads: load i of wave w takes tile rows (i NW + w) RPW .. + RPW - 1 of
-    // each tile of a step (all in one block), from K and from V. Its block
+    // Loads: load i of wave w takes tile rows (w NLD + i) RPW .. + RPW - 1 of
+    // each tile of a step, from K and from V. The wave's block of the tile
     // is one block-table entry, read by a scalar load one step ahead; the
     // buffer resources are zero bytes long for blocks past the end and V
     // rows at or past kmax read past the block, so those arrive as zeros.
@@ -503,12 +503,16 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
     // math.
     constexpr uint32_t kBlockBytes = (uint32_t)(kBS * D * sizeof(T));
     const int lp = lane % KCH;                        // LDS position in the row
-    int wrow[kMaxLoadsPerTile], bw[kMaxLoadsPerTile], lrow[kMaxLoadsPerTile], koff[kMaxLoadsPerTile],
+    // A wave's NLD loads of a tile take NLD x RPW consecutive rows, which lie
+    // in one block of the tile (block bw), so one block id and one pair of
+    // buffer resources serve them all.
+    static_assert(16 % (NLD * RPW) == 0, "a wave's loads of a tile lie in one block");
+    const int bw = w * NLD * RPW / 16;
+    int wrow[kMaxLoadsPerTile], lrow[kMaxLoadsPerTile], koff[kMaxLoadsPerTile],
         voff[kMaxLoadsPerTile];                       // per load i < NLD
 #pragma unroll
     for (int i = 0; i < NLD; ++i) {
-      wrow[i] = (i * NW + w) * RPW;                   // first tile row load i writes
-      bw[i] = wrow[i] / 16;                           // its block within the tile
+      wrow[i] = (w * NLD + i) * RPW;                  // first tile row load i writes
       lrow[i] = (wrow[i] + lane / KCH) % 16;          // this lane's row in the block
       koff[i] = (lrow[i] * D + (lp ^ lrow[i]) * 8) * (int)sizeof(T);
       voff[i] = (lrow[i] * D + (lp ^ (2 * (lrow[i] & 7))) * 8) * (int)sizeof(T);
@@ -518,31 +522,29 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
     // rather than behind the vector loads in flight.
     const __attribute__((address_space(4))) int32_t* bt_const =
         (const __attribute__((address_space(4))) int32_t*)(uintptr_t)bt_row;
-    auto block_id = [&](int u, int i) {               // physical block of load i's block of tile u
-      const int blk = __builtin_amdgcn_readfirstlane(min(u * TB + bw[i], nblk - 1));
+    auto block_id = [&](int u) {                      // physical block of the wave's block of tile u
+      const int blk = __builtin_amdgcn_readfirstlane(min(u * TB + bw, nblk - 1));
       int id = bt_const[blk];
       if ((uint64_t)(int64_t)id >= (uint64_t)P.NB) id = 0;  // out-of-range ids read block 0
       return id;
     };
-    int id_next[KS][NLD];
+    int id_next[KS];
 #pragma unroll
-    for (int j = 0; j < KS; ++j)
-#pragma unroll
-      for (int i = 0; i < NLD; ++i) id_next[j][i] = block_id(j, i);
+    for (int j = 0; j < KS; ++j) id_next[j] = block_id(j);
     auto fetch = [&](int step, u32x4* k_next, u32x4* v_next) {  // the step's tiles into an LDS slot
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
         const int u = step * KS + j;
+        const int id = id_next[j];
+        id_next[j] = block_id(u + KS);
+        const int blk = u * TB + bw;
+        const bool ok = blk < nblk;
+        const int64_t off = ok ? (int64_t)id * block_elems : 0;
+        const uint32_t n = ok ? kBlockBytes : 0u;
+        const __amdgpu_buffer_rsrc_t kr = block_rsrc(kbase + off, n);
+        const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + off, n);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
-          const int id = id_next[j][i];
-          id_next[j][i] = block_id(u + KS, i);
-          const int blk = u * TB + bw[i];
-          const bool ok = blk < nblk;
-          const int64_t off = ok ? (int64_t)id * block_elems : 0;
-          const uint32_t n = ok ? kBlockBytes : 0u;
-          const __amdgpu_buffer_rsrc_t kr = block_rsrc(kbase + off, n);
-          const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + off, n);
           const int rows = j * TCH + wrow[i] * KCH;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(k_next + rows),
                                                    16, koff[i], 0, 0, 0);
