@@ -104,6 +104,10 @@ __device__ __forceinline__ void lds_barrier() {
 // Most 16-byte loads one lane makes per K (or V) tile in any launch shape.
 constexpr int kMaxLoadsPerTile = 4;
 
+// Growth of a row's max (log2 units) below which the online softmax keeps
+// its reference max: P stays below 2^8.
+constexpr float kLazyRescale = 8.f;
+
 struct PrefillParams {
   const void* q;
   const void* k;
@@ -631,10 +635,10 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
     // rescale of the accumulators), P rounded to the 16-bit type, P.V. The
     // code runs straight through but for two branches: the causal mask, only
     // on tiles that reach past the wave's smallest position (masked scores
-    // become -inf), and the rescale, skipped when no row's max grew (rare once
-    // the maxima settle). P and the P.V products of both N-tiles are then one
-    // basic block, in which the exponentials of one N-tile issue while the
-    // matrix cores run the products of the other.
+    // become -inf), and the rescale, skipped unless some row's max outgrew
+    // its reference (rare once the maxima settle). P and the P.V products of
+    // both N-tiles are then one basic block, in which the exponentials of one
+    // N-tile issue while the matrix cores run the products of the other.
     auto tile_math = [&](const u32x4* kt, const u32x4* vt, int t) __attribute__((always_inline)) {
       f32x4 sc[NTW][TB];
       qk_tile(kt, sc);
@@ -658,12 +662,18 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) mx = fmaxf(mx, sc[jj][b][i]);
         mx = rows_max(mx);
-        // A row with no visible key so far keeps max -inf (with a key split,
-        // a key group's first tile can hide every key from a row): alpha is
+        // The reference m (log2 units) moves only when the row's max exceeds
+        // it by more than kLazyRescale: P = 2^(score - m) then stays below
+        // 2^kLazyRescale, as exact in bf16 and fp16 as below 1, and the
+        // rescale of the accumulators is rare after a row's first tiles. A
+        // row with no visible key so far keeps m = -inf (with a key split, a
+        // key group's first tile can hide every key from a row): alpha is
         // then 1, and P is taken against 0 (every score of the row is -inf).
-        const float mnew = fmaxf(m[jj], mx * s2);
-        alpha[jj] = m[jj] == mnew ? 1.f : fast_exp2(m[jj] - mnew);
-        grew |= alpha[jj] != 1.f;
+        const float mt = mx * s2;
+        const bool moves = mt > m[jj] + kLazyRescale;
+        const float mnew = moves ? mt : m[jj];
+        alpha[jj] = moves ? fast_exp2(m[jj] - mnew) : 1.f;
+        grew |= moves;
         m[jj] = mnew;
         mb[jj] = mnew == -INFINITY ? 0.f : mnew;
       }
