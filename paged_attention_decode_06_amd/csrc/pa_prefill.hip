@@ -2,6 +2,7 @@
 // the kernel and its C ABI entry point (pa_prefill, declared in pa_decode.h).
 
 #include <algorithm>
+#include <cfloat>
 #include <type_traits>
 #include <utility>
 
@@ -499,13 +500,15 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
     // Loads: load i of wave w takes tile rows (w NLD + i) RPW .. + RPW - 1 of
     // each tile of a step, from K and from V. The wave's block of the tile
     // is one block-table entry, read by a scalar load one step ahead; the
-    // buffer resources are zero bytes long for blocks past the end and V
-    // rows at or past kmax read past the block, so those arrive as zeros.
+    // buffer resources are zero bytes long for blocks past the end, and a V
+    // resource ends at the block's last row below kmax (a lane's 16 bytes
+    // lie in one row), so those rows arrive as zeros with no per-lane test.
     // Every wave issues the same 2 KS NLD loads per step; a step's loads are
     // waited for (vmcnt, counted by hand: the compiler does not track writes
     // to LDS that come from loads) at the end of the iteration before its
     // math.
-    constexpr uint32_t kBlockBytes = (uint32_t)(kBS * D * sizeof(T));
+    constexpr uint32_t kRowBytes = (uint32_t)(D * sizeof(T));
+    constexpr uint32_t kBlockBytes = kBS * kRowBytes;
     const int lp = lane % KCH;                        // LDS position in the row
     // A wave's NLD loads of a tile take NLD x RPW consecutive rows, which lie
     // in one block of the tile (block bw), so one block id and one pair of
@@ -545,16 +548,16 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
         const bool ok = blk < nblk;
         const int64_t off = ok ? (int64_t)id * block_elems : 0;
         const uint32_t n = ok ? kBlockBytes : 0u;
+        const uint32_t nv = ok ? (uint32_t)min(max(kmax - blk * kBS, 0), kBS) * kRowBytes : 0u;  // rows below kmax
         const __amdgpu_buffer_rsrc_t kr = block_rsrc(kbase + off, n);
-        const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + off, n);
+        const __amdgpu_buffer_rsrc_t vr = block_rsrc(vbase + off, nv);
 #pragma unroll
         for (int i = 0; i < NLD; ++i) {
           const int rows = j * TCH + wrow[i] * KCH;
           __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (__attribute__((address_space(3))) void*)(k_next + rows),
                                                    16, koff[i], 0, 0, 0);
           __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (__attribute__((address_space(3))) void*)(v_next + rows),
-                                                   16, blk * kBS + lrow[i] < kmax ? voff[i] : (int)kBlockBytes,
-                                                   0, 0, 0);
+                                                   16, voff[i], 0, 0, 0);
         }
       }
     };
@@ -668,14 +671,15 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
         // rescale of the accumulators is rare after a row's first tiles. A
         // row with no visible key so far keeps m = -inf (with a key split, a
         // key group's first tile can hide every key from a row): alpha is
-        // then 1, and P is taken against 0 (every score of the row is -inf).
+        // then 1, and P is taken against -FLT_MAX (every score of the row is
+        // -inf, so P is still 0).
         const float mt = mx * s2;
         const bool moves = mt > m[jj] + kLazyRescale;
         const float mnew = moves ? mt : m[jj];
         alpha[jj] = moves ? fast_exp2(m[jj] - mnew) : 1.f;
         grew |= moves;
         m[jj] = mnew;
-        mb[jj] = mnew == -INFINITY ? 0.f : mnew;
+        mb[jj] = fmaxf(mnew, -FLT_MAX);
       }
       if (__builtin_amdgcn_ballot_w64(grew)) {
 #pragma unroll
