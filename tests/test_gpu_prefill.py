@@ -212,17 +212,19 @@ def test_prefill_rejects_f32(dev):
 WIDE = [None, 160]
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("mb", WIDE)
-def test_prefill_large_grid_every_token(dev, mb):
-    """More than 512 workgroups (the many-workgroup launch shapes), every token compared."""
+def test_prefill_large_grid_every_token(dev, mb, dtype):
+    """More than 512 workgroups (the many-workgroup launch shapes), every token
+    compared, with bf16 and with fp16 caches."""
     rng = np.random.default_rng(58)
     S = 40
     ctx = rng.integers(0, 300, size=S)
     ql = rng.integers(100, 129, size=S)
-    x = W.make_prefill_inputs(W.PREFILL_WORKLOADS[2], seed=58, context_lens=ctx, query_lens=ql,
-                              max_blocks_per_seq=mb)
-    say(f"prefill large grid: {S} seqs, {x.num_query_tokens} tokens, table width {x.max_blocks_per_seq}")
-    check_all(x, run(x, dev), "large grid")
+    cfg = dataclasses.replace(W.PREFILL_WORKLOADS[2], dtype=dtype)
+    x = W.make_prefill_inputs(cfg, seed=58, context_lens=ctx, query_lens=ql, max_blocks_per_seq=mb)
+    say(f"prefill large grid, {dtype}: {S} seqs, {x.num_query_tokens} tokens, table width {x.max_blocks_per_seq}")
+    check_all(x, run(x, dev), f"large grid {dtype}")
 
 
 @pytest.mark.parametrize("mb", WIDE)
