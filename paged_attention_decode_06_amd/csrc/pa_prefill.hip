@@ -831,21 +831,22 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
 //     workgroups still fill the chip with 32-row waves;
 //   D = 128, larger grids: 256 rows per workgroup, 8 waves x 2 N-tiles, no
 //     key split, two steps in flight (96 KB; 1.02x one step);
-//   D = 128, larger grids over tables of at most kPrefillShortTable tokens
-//     (short prompts): 128 rows, 4 waves x 2 N-tiles, 64 KB, two workgroups
-//     per CU, so that one workgroup's prologue and output stores overlap the
-//     other's steps (1.02-1.09x on prompts of 256-2048 tokens; 0.94-0.97x
-//     on long contexts, where the 8-wave form shares each K/V tile among
-//     twice the rows);
+//   D = 128, larger grids over tables of at most kPrefillShortTable tokens:
+//     128 rows, 4 waves x 2 N-tiles, 64 KB, two workgroups per CU, so that
+//     one workgroup's prologue and output stores overlap the other's steps
+//     (1.04-1.14x on prompts of up to 1024 tokens, 1.06-1.12x on 128 short
+//     chunks behind prefixes of up to 6K tokens, 0.98-1.03x on long chunks
+//     in such tables; on longer contexts the 8-wave form, which shares each
+//     K/V tile among twice the rows, was 1.03-1.06x faster);
 //   D = 256: 128 rows per workgroup, 8 waves x 1 N-tile (the register budget
 //     of the wider rows), no key split.
-// The P.V products take a tile's blocks in pairs, as 16x16x32 MFMAs
-// (one-block tiles would make them 16x16x16 ones, which do half the work in
-// the same issue time).
+// The P.V products take a tile's four blocks as two pairs, as 16x16x32
+// MFMAs (one-block tiles would make them 16x16x16 ones, which do half the
+// work in the same issue time).
 constexpr int kPrefillRows = 64;       // rows per workgroup: a lower bound over the launch shapes
 constexpr int kPrefillMaxNW = 8;       // waves per workgroup, largest launch shape
 constexpr int64_t kPrefillSmallGrid = 512;
-constexpr int64_t kPrefillShortTable = 2048;
+constexpr int64_t kPrefillShortTable = 8192;
 
 // A launch shape: D, NW waves, NTW N-tiles per wave, TB-block key tiles,
 // SHD steps in flight, KS key groups.

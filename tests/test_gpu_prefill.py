@@ -206,10 +206,10 @@ def test_prefill_rejects_f32(dev):
         run(x, dev)
 
 
-# Table widths for the many-workgroup tests: the natural one (at most 2048
-# tokens: the 4-wave short-table shape) and 160 blocks (2560 tokens: the
+# Table widths for the many-workgroup tests: the natural one (at most 8192
+# tokens: the 4-wave short-table shape) and 600 blocks (9600 tokens: the
 # 8-wave shape).
-WIDE = [None, 160]
+WIDE = [None, 600]
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
