@@ -448,15 +448,6 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones8[i] = (T)1.0f;
 
-  // The QK scores of N-tile jj from K operands ka.
-  auto qk_scores = [&](const tx8 (&ka)[TB][KK], int jj, f32x4 (&sc)[TB]) {
-#pragma unroll
-    for (int b = 0; b < TB; ++b) {
-      sc[b] = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KK; ++kk) sc[b] = H16<T>::mma32(ka[b][kk], qv[jj][kk], sc[b]);
-    }
-  };
   auto pack_p2 = [&](const T (&p0)[4], const T (&p1)[4]) {  // two blocks of P as one B operand, keys 4grp+i, 16+4grp+i
     tx8 pv;
 #pragma unroll
@@ -571,50 +562,44 @@ __global__ __launch_bounds__(NW * 64, 2) void pa_prefill_h16(PrefillParams P) {
       vlo[mt] = (R * KCH + 2 * (mt ^ (R & 7)) + ((g >> 1) & 1)) * 16 + (g & 1) * 8;
     }
     auto qk_tile = [&](const u32x4* kt, f32x4 (&sc)[NTW][TB]) {  // QK scores of the K tile at kt
-      if constexpr (D == 256) {
-        // head_dim 256: a tile's K operands would take 128 registers, so they
-        // are read one block ahead (two blocks of 32 registers in turn), the
-        // reads of block b + 1 interleaved with the products of block b
-        // (sched_group_barrier: one MFMA, one LDS read). Left to itself the
-        // compiler read each operand just before its product and waited on it.
-        tx8 k0[KK], k1[KK];
-        auto read_k = [&](int b, tx8 (&ka)[KK]) __attribute__((always_inline)) {
+      // The K operands are read one block ahead (two sets of KK registers in
+      // turn), the reads of block b + 1 interleaved with the products of
+      // block b (sched_group_barrier: one MFMA per N-tile, one LDS read). At
+      // head_dim 256 a whole tile's operands would take 128 registers and the
+      // compiler read each just before its product and waited on it; at 128
+      // it read them all up front (64 registers) and waited on the first.
+      tx8 k0[KK], k1[KK];
+      auto read_k = [&](int b, tx8 (&ka)[KK]) __attribute__((always_inline)) {
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) ka[kk] = __builtin_bit_cast(tx8, kt[klo[kk] + b * 16 * KCH]);
-        };
-        auto mma_k = [&](int b, const tx8 (&ka)[KK]) __attribute__((always_inline)) {
-          sc[0][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        for (int kk = 0; kk < KK; ++kk) ka[kk] = __builtin_bit_cast(tx8, kt[klo[kk] + b * 16 * KCH]);
+      };
+      auto mma_k = [&](int b, const tx8 (&ka)[KK]) __attribute__((always_inline)) {
 #pragma unroll
-          for (int kk = 0; kk < KK; ++kk) sc[0][b] = H16<T>::mma32(ka[kk], qv[0][kk], sc[0][b]);
-        };
-        read_k(0, k0);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int jj = 0; jj < NTW; ++jj) sc[jj][b] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int b = 0; b < TB; ++b) {
-          if (b % 2 == 0) {
-            mma_k(b, k0);
-            if (b + 1 < TB) read_k(b + 1, k1);
-          } else {
-            mma_k(b, k1);
-            if (b + 1 < TB) read_k(b + 1, k0);
-          }
-          if (b + 1 < TB) {
+        for (int kk = 0; kk < KK; ++kk)
 #pragma unroll
-            for (int i = 0; i < KK; ++i) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
+          for (int jj = 0; jj < NTW; ++jj) sc[jj][b] = H16<T>::mma32(ka[kk], qv[jj][kk], sc[jj][b]);
+      };
+      read_k(0, k0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int b = 0; b < TB; ++b) {
+        if (b % 2 == 0) {
+          mma_k(b, k0);
+          if (b + 1 < TB) read_k(b + 1, k1);
+        } else {
+          mma_k(b, k1);
+          if (b + 1 < TB) read_k(b + 1, k0);
         }
-      } else {
-        tx8 ka[TB][KK];
+        if (b + 1 < TB) {
 #pragma unroll
-        for (int b = 0; b < TB; ++b)
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk) ka[b][kk] = __builtin_bit_cast(tx8, kt[klo[kk] + b * 16 * KCH]);
-#pragma unroll
-        for (int jj = 0; jj < NTW; ++jj) qk_scores(ka, jj, sc[jj]);
+          for (int i = 0; i < KK; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, NTW, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     };
     // P.V products (and row sums). V^T operand of M-tile mt (head dims
