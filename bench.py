@@ -703,7 +703,8 @@ def main(argv=None):
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the decode path runs on a single MI355X and has no "
-              "multi-GPU mode (see the sharding notes in the design document). Run with --gpus 1.",
+              "multi-GPU mode (across GPUs it would shard by sequence, or by KV head, each GPU running "
+              "the same kernels on its share). Run with --gpus 1.",
               file=sys.stderr)
         return 2
 
